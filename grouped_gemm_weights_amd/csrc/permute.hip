@@ -1,0 +1,223 @@
+// moe_permute: per-expert counts, offsets, the stable expert-major
+// permutation and the row gather.
+//
+// The R = T*k assignments are cut into chunks (at most kMaxChunks of them).
+//  1. hist:    one block per chunk builds an LDS histogram of its expert ids.
+//  2. scan:    one block turns the chunk histograms into counts[e],
+//              offsets[e] (exclusive scan over e) and chunk_base[c][e] =
+//              offsets[e] + (rows of expert e in chunks before c).
+//  3. scatter: one wave per chunk walks its assignments in order, 64 at a
+//              time; lanes holding the same expert find each other with one
+//              ballot per id bit, so an assignment's rank among equal ids of
+//              its batch is a popcount, and a per-expert LDS cursor carries
+//              the running position across batches.  No atomics decide an
+//              order, so the permutation is the stable counting sort.
+//  4. gather:  x_perm[r] = x[src_of[r] / k] with 16-byte vector copies.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxChunks = 256;
+
+struct Chunking {
+  int chunk;     // assignments per chunk (multiple of 64)
+  int n_chunks;  // <= kMaxChunks
+};
+
+Chunking chunking(int64_t R) {
+  int64_t c = ceil_div64(R, kMaxChunks);
+  c = ceil_div64(c, 64) * 64;
+  if (c < 64) c = 64;
+  Chunking ch;
+  ch.chunk = static_cast<int>(c);
+  ch.n_chunks = static_cast<int>(ceil_div64(R, c));
+  return ch;
+}
+
+size_t permute_ws_bytes(int64_t R, int E) {
+  const Chunking ch = chunking(R);
+  // chunk_counts and chunk_base, each [n_chunks][E]
+  return align_up(2 * static_cast<size_t>(ch.n_chunks) * E * sizeof(int32_t), 256);
+}
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx, int R, int E,
+                                                   int chunk, int32_t* __restrict__ chunk_counts,
+                                                   int32_t* status) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * chunk;
+  const int a1 = min(R, a0 + chunk);
+  bool bad = false;
+  for (int a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
+    const int e = idx[a];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    else bad = true;
+  }
+  if (bad) status_or(status, MOE_STATUS_BAD_EXPERT_ID);
+  __syncthreads();
+  int32_t* out = chunk_counts + static_cast<int64_t>(blockIdx.x) * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = hist[e];
+}
+
+// One block of MOE_MAX_E threads; thread e owns expert e.
+__global__ __launch_bounds__(MOE_MAX_E) void scan_kernel(const int32_t* __restrict__ chunk_counts,
+                                                         int n_chunks, int E,
+                                                         int32_t* __restrict__ chunk_base,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int32_t s[MOE_MAX_E];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      const int64_t i = static_cast<int64_t>(c) * E + e;
+      const int32_t v = chunk_counts[i];
+      chunk_base[i] = run;
+      run += v;
+    }
+    counts[e] = run;
+  }
+  s[e] = e < E ? run : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the experts
+  for (int off = 1; off < MOE_MAX_E; off <<= 1) {
+    const int32_t add = e >= off ? s[e - off] : 0;
+    __syncthreads();
+    s[e] += add;
+    __syncthreads();
+  }
+  const int32_t excl = s[e] - (e < E ? run : 0);
+  if (e < E) {
+    offsets[e] = excl;
+    for (int c = 0; c < n_chunks; ++c) chunk_base[static_cast<int64_t>(c) * E + e] += excl;
+  }
+  if (e == E - 1) offsets[E] = s[e];
+}
+
+__global__ __launch_bounds__(kWave) void scatter_kernel(const int32_t* __restrict__ idx, int R,
+                                                        int E, int chunk,
+                                                        const int32_t* __restrict__ chunk_base,
+                                                        int32_t* __restrict__ row_of,
+                                                        int32_t* __restrict__ src_of) {
+  extern __shared__ int32_t cursor[];
+  const int lane = threadIdx.x;
+  const int32_t* base = chunk_base + static_cast<int64_t>(blockIdx.x) * E;
+  for (int e = lane; e < E; e += kWave) cursor[e] = base[e];
+  __syncthreads();
+  const int nbits = E > 1 ? 32 - __builtin_clz(static_cast<unsigned>(E - 1)) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int a0 = blockIdx.x * chunk;
+  const int a1 = min(R, a0 + chunk);
+  for (int ab = a0; ab < a1; ab += kWave) {
+    const int a = ab + lane;
+    int e = a < a1 ? idx[a] : -1;
+    const bool ok = e >= 0 && e < E;
+    uint64_t same = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const uint64_t bb = __ballot(bit);
+      same &= bit ? bb : ~bb;
+    }
+    int pos = 0;
+    if (ok) {
+      const int rank = __popcll(same & lt_mask);
+      pos = cursor[e] + rank;
+    }
+    // all lanes have read their cursor before the group leaders advance it
+    __builtin_amdgcn_wave_barrier();
+    if (ok) {
+      const int leader = 63 - __clzll(same);
+      if (lane == leader) cursor[e] += __popcll(same);
+      row_of[a] = pos;
+      src_of[pos] = a;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// One wave per row; 16-byte copies when the row is a whole number of 16-byte words.
+__global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ x,
+                                                     const int32_t* __restrict__ src_of, int R,
+                                                     int T, int k, int64_t row_bytes,
+                                                     char* __restrict__ x_perm) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (r >= R) return;
+  const int a = src_of[r];
+  // rows past offsets[E] are unwritten when an id was out of range: skip them
+  if (a < 0 || a >= R) return;
+  const int t = a / k;
+  if (t >= T) return;
+  const char* src = x + static_cast<int64_t>(t) * row_bytes;
+  char* dst = x_perm + static_cast<int64_t>(r) * row_bytes;
+  if ((row_bytes & 15) == 0) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
+    const int64_t n = row_bytes >> 4;
+    for (int64_t i = lane; i < n; i += kWave) d4[i] = s4[i];
+  } else {
+    const uint16_t* s2 = reinterpret_cast<const uint16_t*>(src);
+    uint16_t* d2 = reinterpret_cast<uint16_t*>(dst);
+    const int64_t n = row_bytes >> 1;
+    for (int64_t i = lane; i < n; i += kWave) d2[i] = s2[i];
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_permute_workspace_size(int T, int E, int k, size_t* bytes) {
+  using namespace moe;
+  if (!bytes || T < 0 || E < 1 || k < 1) return fail(MOE_ERR_ARG, "moe_permute_workspace_size: bad arguments");
+  *bytes = permute_ws_bytes(static_cast<int64_t>(T) * k, E);
+  return MOE_OK;
+}
+
+extern "C" int moe_permute(const int32_t* topk_idx, int T, int E, int k, const void* x, int H,
+                           moe_dtype dtype, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                           int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes,
+                           int32_t* status, moe_stream_t stream) {
+  using namespace moe;
+  if (T < 0 || E < 1 || k < 1 || H < 1 || (dtype != MOE_F32 && dtype != MOE_BF16))
+    return fail(MOE_ERR_ARG, "moe_permute: bad sizes T=%d E=%d k=%d H=%d", T, E, k, H);
+  if (E > MOE_MAX_E) return fail(MOE_ERR_UNSUPPORTED, "moe_permute: E=%d above %d", E, MOE_MAX_E);
+  const int64_t R64 = static_cast<int64_t>(T) * k;
+  if (R64 > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_permute: T*k too large");
+  const int R = static_cast<int>(R64);
+  if (!counts || !offsets || (R > 0 && (!topk_idx || !row_of || !src_of)))
+    return fail(MOE_ERR_ARG, "moe_permute: null pointer");
+  if (x_perm && R > 0 && !x) return fail(MOE_ERR_ARG, "moe_permute: x_perm given without x");
+  const size_t need = permute_ws_bytes(R, E);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "moe_permute: workspace %zu < %zu bytes", ws_bytes, need);
+
+  hipStream_t s = as_stream(stream);
+  const Chunking ch = R > 0 ? chunking(R) : Chunking{64, 0};
+  int32_t* chunk_counts = static_cast<int32_t*>(ws);
+  int32_t* chunk_base = chunk_counts + static_cast<int64_t>(ch.n_chunks) * E;
+  const size_t lds = static_cast<size_t>(E) * sizeof(int32_t);
+
+  if (ch.n_chunks > 0) {
+    hipLaunchKernelGGL(hist_kernel, dim3(ch.n_chunks), dim3(256), lds, s, topk_idx, R, E,
+                       ch.chunk, chunk_counts, status);
+    MOE_LAUNCH_CHECK("moe_permute: hist launch");
+  }
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(MOE_MAX_E), 0, s, chunk_counts, ch.n_chunks, E,
+                     chunk_base, counts, offsets);
+  MOE_LAUNCH_CHECK("moe_permute: scan launch");
+  if (ch.n_chunks > 0) {
+    hipLaunchKernelGGL(scatter_kernel, dim3(ch.n_chunks), dim3(kWave), lds, s, topk_idx, R, E,
+                       ch.chunk, chunk_base, row_of, src_of);
+    MOE_LAUNCH_CHECK("moe_permute: scatter launch");
+  }
+  if (x_perm && R > 0) {
+    const int64_t row_bytes = static_cast<int64_t>(H) * elem_size(dtype);
+    hipLaunchKernelGGL(gather_kernel, dim3(ceil_div(R, 4)), dim3(256), 0, s,
+                       static_cast<const char*>(x), src_of, R, T, k, row_bytes,
+                       static_cast<char*>(x_perm));
+    MOE_LAUNCH_CHECK("moe_permute: gather launch");
+  }
+  return MOE_OK;
+}

@@ -1,0 +1,200 @@
+// Merged weight buffer management: the slot map, the merge of the local
+// experts and the copy-engine prefetch of the remote ones.  Also the small
+// event / error helpers of the C ABI.
+//
+// A merged buffer half holds n_slots expert blocks in one contiguous
+// allocation; the expert set of a layer (ascending ids) fills slots 0..n-1 in
+// order.  moe_merge_weights writes the device slot map with a kernel whose
+// arguments carry the map (so it is ordered on the stream like the copies and
+// needs no host staging buffer that could be overwritten while in flight),
+// then copies the local pool's experts into their slots; moe_prefetch_layer
+// copies the remote pool's experts.  Runs of consecutive ids that sit in
+// consecutive slots and consecutive pool positions go out as one copy.  With
+// MOE_COPY_SDMA a device-to-device copy is issued as
+// hipMemcpyDeviceToDeviceNoCU, which the runtime executes on an SDMA engine
+// and never on the compute units (DWDP explainer, "stay data-parallel" panel:
+// the pull runs on the copy engine, off the compute units).
+#include <vector>
+
+#include "common.h"
+
+namespace moe {
+
+std::string& last_error() {
+  static thread_local std::string s;
+  return s;
+}
+
+namespace {
+
+constexpr int kSlotIdsPerLaunch = 256;
+
+struct SlotChunk {
+  int32_t ids[kSlotIdsPerLaunch];
+  int32_t n;
+  int32_t first_slot;
+};
+
+__global__ void slot_fill_kernel(int32_t* slot_of, int E) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) slot_of[e] = -1;
+}
+
+__global__ void slot_set_kernel(int32_t* slot_of, SlotChunk c) {
+  const int i = threadIdx.x;
+  if (i < c.n) slot_of[c.ids[i]] = c.first_slot + i;
+}
+
+int check_ids(const char* who, const int32_t* ids, int n, const moe_wbuf* dst) {
+  if (!dst || !dst->base || dst->expert_bytes <= 0 || dst->n_experts < 1 || dst->n_slots < 0)
+    return fail(MOE_ERR_ARG, "%s: bad merged buffer", who);
+  if (n < 0 || n > dst->n_slots)
+    return fail(MOE_ERR_ARG, "%s: %d ids for %d slots", who, n, dst->n_slots);
+  if (n > 0 && !ids) return fail(MOE_ERR_ARG, "%s: null ids", who);
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= dst->n_experts)
+      return fail(MOE_ERR_ARG, "%s: id %d outside [0, %d)", who, ids[i], dst->n_experts);
+    if (i > 0 && ids[i] <= ids[i - 1])
+      return fail(MOE_ERR_ARG, "%s: ids not strictly ascending at %d", who, i);
+  }
+  return MOE_OK;
+}
+
+int check_pool(const char* who, const moe_pool* p, const moe_wbuf* dst) {
+  if (!p || !p->base || p->n_experts < 0 || p->first_expert < 0)
+    return fail(MOE_ERR_ARG, "%s: bad pool", who);
+  if (p->expert_bytes != dst->expert_bytes)
+    return fail(MOE_ERR_ARG, "%s: pool expert_bytes %lld != buffer %lld", who,
+                static_cast<long long>(p->expert_bytes), static_cast<long long>(dst->expert_bytes));
+  return MOE_OK;
+}
+
+int copy_kind(const char* who, const void* src, int copy_mode, hipMemcpyKind* kind) {
+  if (copy_mode != MOE_COPY_SDMA && copy_mode != MOE_COPY_ANY)
+    return fail(MOE_ERR_ARG, "%s: bad copy_mode %d", who, copy_mode);
+  if (copy_mode == MOE_COPY_ANY) {
+    *kind = hipMemcpyDefault;
+    return MOE_OK;
+  }
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, src);
+  if (e != hipSuccess) return hip_fail(e, "hipPointerGetAttributes(pool)");
+  *kind = (attr.type == hipMemoryTypeHost) ? hipMemcpyHostToDevice : hipMemcpyDeviceToDeviceNoCU;
+  return MOE_OK;
+}
+
+// Copy the experts of ids that the pool holds into their slots; returns bytes issued.
+int copy_pool_experts(const moe_pool* p, const int32_t* ids, int n, moe_wbuf* dst,
+                      hipStream_t s, hipMemcpyKind kind) {
+  const int64_t eb = dst->expert_bytes;
+  const int64_t lo = p->first_expert, hi = lo + p->n_experts;
+  auto in_pool = [&](int32_t e) { return e >= lo && e < hi; };
+  int i = 0;
+  while (i < n) {
+    if (!in_pool(ids[i])) {
+      ++i;
+      continue;
+    }
+    int j = i + 1;
+    while (j < n && in_pool(ids[j]) && ids[j] == ids[j - 1] + 1) ++j;
+    const char* src = static_cast<const char*>(p->base) + (ids[i] - lo) * eb;
+    char* to = static_cast<char*>(dst->base) + static_cast<int64_t>(i) * eb;
+    MOE_HIP_CHECK(hipMemcpyAsync(to, src, static_cast<size_t>(j - i) * eb, kind, s));
+    i = j;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_merge_weights(const moe_pool* local, const int32_t* ids_host, int n_ids,
+                                 moe_wbuf* dst, moe_stream_t stream, moe_event_t wait_free,
+                                 moe_event_t ready, int copy_mode) {
+  using namespace moe;
+  int rc = check_ids("moe_merge_weights", ids_host, n_ids, dst);
+  if (rc) return rc;
+  if (!dst->slot_of) return fail(MOE_ERR_ARG, "moe_merge_weights: null slot map");
+  rc = check_pool("moe_merge_weights", local, dst);
+  if (rc) return rc;
+  hipMemcpyKind kind;
+  rc = copy_kind("moe_merge_weights", local->base, copy_mode, &kind);
+  if (rc) return rc;
+  hipStream_t s = as_stream(stream);
+  if (wait_free) MOE_HIP_CHECK(hipStreamWaitEvent(s, as_event(wait_free), 0));
+  const int E = dst->n_experts;
+  hipLaunchKernelGGL(slot_fill_kernel, dim3(ceil_div(E, 256)), dim3(256), 0, s, dst->slot_of, E);
+  MOE_LAUNCH_CHECK("moe_merge_weights: slot fill");
+  for (int i0 = 0; i0 < n_ids; i0 += kSlotIdsPerLaunch) {
+    SlotChunk c;
+    c.n = std::min(kSlotIdsPerLaunch, n_ids - i0);
+    c.first_slot = i0;
+    for (int i = 0; i < c.n; ++i) c.ids[i] = ids_host[i0 + i];
+    hipLaunchKernelGGL(slot_set_kernel, dim3(1), dim3(kSlotIdsPerLaunch), 0, s, dst->slot_of, c);
+    MOE_LAUNCH_CHECK("moe_merge_weights: slot set");
+  }
+  rc = copy_pool_experts(local, ids_host, n_ids, dst, s, kind);
+  if (rc) return rc;
+  if (ready) MOE_HIP_CHECK(hipEventRecord(as_event(ready), s));
+  return MOE_OK;
+}
+
+extern "C" int moe_prefetch_layer(const moe_pool* remote, const int32_t* ids_host, int n_ids,
+                                  moe_wbuf* dst, moe_stream_t copy_stream, moe_event_t wait_free,
+                                  moe_event_t ready, int copy_mode) {
+  using namespace moe;
+  int rc = check_ids("moe_prefetch_layer", ids_host, n_ids, dst);
+  if (rc) return rc;
+  rc = check_pool("moe_prefetch_layer", remote, dst);
+  if (rc) return rc;
+  hipMemcpyKind kind;
+  rc = copy_kind("moe_prefetch_layer", remote->base, copy_mode, &kind);
+  if (rc) return rc;
+  hipStream_t s = as_stream(copy_stream);
+  if (wait_free) MOE_HIP_CHECK(hipStreamWaitEvent(s, as_event(wait_free), 0));
+  rc = copy_pool_experts(remote, ids_host, n_ids, dst, s, kind);
+  if (rc) return rc;
+  if (ready) MOE_HIP_CHECK(hipEventRecord(as_event(ready), s));
+  return MOE_OK;
+}
+
+extern "C" int moe_event_create(moe_event_t* ev, int timing) {
+  using namespace moe;
+  if (!ev) return fail(MOE_ERR_ARG, "moe_event_create: null");
+  hipEvent_t e;
+  MOE_HIP_CHECK(hipEventCreateWithFlags(&e, timing ? hipEventDefault : hipEventDisableTiming));
+  *ev = reinterpret_cast<moe_event_t>(e);
+  return MOE_OK;
+}
+
+extern "C" int moe_event_destroy(moe_event_t ev) {
+  using namespace moe;
+  if (!ev) return MOE_OK;
+  MOE_HIP_CHECK(hipEventDestroy(as_event(ev)));
+  return MOE_OK;
+}
+
+extern "C" int moe_event_record(moe_event_t ev, moe_stream_t stream) {
+  using namespace moe;
+  if (!ev) return fail(MOE_ERR_ARG, "moe_event_record: null");
+  MOE_HIP_CHECK(hipEventRecord(as_event(ev), as_stream(stream)));
+  return MOE_OK;
+}
+
+extern "C" int moe_event_elapsed_ms(moe_event_t start, moe_event_t stop, float* ms) {
+  using namespace moe;
+  if (!start || !stop || !ms) return fail(MOE_ERR_ARG, "moe_event_elapsed_ms: null");
+  MOE_HIP_CHECK(hipEventElapsedTime(ms, as_event(start), as_event(stop)));
+  return MOE_OK;
+}
+
+extern "C" int moe_stream_wait_event(moe_stream_t stream, moe_event_t ev) {
+  using namespace moe;
+  if (!ev) return fail(MOE_ERR_ARG, "moe_stream_wait_event: null");
+  MOE_HIP_CHECK(hipStreamWaitEvent(as_stream(stream), as_event(ev), 0));
+  return MOE_OK;
+}
+
+extern "C" const char* moe_last_error(void) { return moe::last_error().c_str(); }
+
+extern "C" const char* moe_version(void) { return "moe-gfx950 0.1"; }

@@ -1,0 +1,202 @@
+"""Host orchestration of the MoE layer forward on one GPU, through the C ABI.
+
+``MoELayer`` owns the device buffers of one layer (PyTorch is used only to
+allocate device memory and to provide streams) and issues the library calls
+of one forward step:
+
+    compute stream:  moe_route -> moe_permute -> (counts to host)
+    copy stream:     moe_merge_weights (local experts + slot map)
+                     -> moe_prefetch_layer (remote experts) -> ready event
+    compute stream:  wait(ready) -> moe_grouped_swiglu -> moe_combine
+                     -> free event (the half may be refilled)
+
+This is the layer step of the DWDP explainer's prefetch-schedule panel with
+the merged buffer of its contiguous-buffer panel; the peers' share of the
+experts is a separate device pool (or pinned host memory) on this GPU.
+Every step of the arithmetic runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .synth import MoEConfig, expert_block_bytes
+
+
+def _dtype_code(cfg: MoEConfig) -> int:
+    return B.MOE_F32 if cfg.dtype == "f32" else B.MOE_BF16
+
+
+def _torch_dtype(cfg: MoEConfig):
+    return torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+
+class MoELayer:
+    """Buffers and streams for one MoE layer of shape ``cfg`` on ``device``.
+
+    ``n_halves`` merged-buffer halves of ``n_slots`` slots each are allocated
+    (two for the double buffer).  The pools are set with ``set_pools`` (device
+    tensors [n, 3*H*I], or pinned host tensors for the remote pool).
+    """
+
+    def __init__(self, cfg: MoEConfig, device="cuda", n_slots: Optional[int] = None,
+                 n_halves: int = 2, compute_stream=None, copy_stream=None,
+                 copy_mode: int = B.MOE_COPY_SDMA):
+        self.cfg = cfg
+        self.dev = torch.device(device)
+        self.copy_mode = copy_mode
+        T, E, k, H, I = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I
+        R = T * k
+        self.R = R
+        self.eb = expert_block_bytes(cfg)
+        self.dt = _dtype_code(cfg)
+        tdt = _torch_dtype(cfg)
+        d = self.dev
+        i32 = dict(dtype=torch.int32, device=d)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=d)
+        self.x = torch.empty((T, H), dtype=tdt, device=d)
+        self.topk_idx = torch.empty((T, k), **i32)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=d)
+        self.counts = torch.empty((E,), **i32)
+        self.offsets = torch.empty((E + 1,), **i32)
+        self.row_of = torch.empty((R,), **i32)
+        self.src_of = torch.empty((R,), **i32)
+        self.x_perm = torch.empty((R, H), dtype=tdt, device=d)
+        self.y_perm = torch.empty((R, H), dtype=torch.float32, device=d)
+        self.y = torch.empty((T, H), dtype=torch.float32, device=d)
+        self.status = torch.zeros((1,), **i32)
+        self.ws_perm_bytes = B.moe_permute_workspace_size(T, E, k)
+        self.ws_perm = torch.empty((max(1, self.ws_perm_bytes),), dtype=torch.uint8, device=d)
+        self.ws_gemm_bytes = B.moe_grouped_swiglu_workspace_size(R, E, H, I, self.dt)
+        self.ws_gemm = torch.empty((self.ws_gemm_bytes,), dtype=torch.uint8, device=d)
+        self.counts_host = torch.empty((E,), dtype=torch.int32, pin_memory=True)
+        self.n_slots = E if n_slots is None else n_slots
+        self.halves = []
+        self.wbufs = []
+        for _ in range(n_halves):
+            base = torch.empty((self.n_slots, self.eb), dtype=torch.uint8, device=d)
+            slot_of = torch.full((E,), -1, **i32)
+            self.halves.append((base, slot_of))
+            self.wbufs.append(B.wbuf(base, self.eb, self.n_slots, E, slot_of))
+        self.compute_stream = compute_stream or torch.cuda.Stream(device=d)
+        self.copy_stream = copy_stream or torch.cuda.Stream(device=d)
+        self.ready = [B.moe_event_create(False) for _ in range(n_halves)]
+        self.free = [B.moe_event_create(False) for _ in range(n_halves)]
+        self.local_pool = None
+        self.remote_pool = None
+        self.last_ids = None
+        torch.cuda.current_stream(d).synchronize()   # buffers initialised on torch's stream
+
+    # ------------------------------------------------------------------ setup
+    def set_pools(self, local: torch.Tensor, remote: torch.Tensor) -> None:
+        """local: experts [0, n_local); remote: experts [n_local, E); each [n, 3*H*I]."""
+        cfg = self.cfg
+        assert local.shape[0] == cfg.n_local and remote.shape[0] == cfg.E - cfg.n_local
+        assert local.is_contiguous() and remote.is_contiguous()
+        self._local_t, self._remote_t = local, remote
+        self.local_pool = B.pool(local, self.eb, 0, cfg.n_local)
+        self.remote_pool = B.pool(remote, self.eb, cfg.n_local, cfg.E - cfg.n_local)
+        torch.cuda.current_stream(self.dev).synchronize()
+
+    def set_inputs(self, x, logits) -> None:
+        """x: numpy [T,H] (float32, or uint16 bf16 bits) or torch; logits numpy f32 [T,E] or torch."""
+        if isinstance(x, np.ndarray):
+            if x.dtype == np.uint16:
+                x = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+            else:
+                x = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+        if isinstance(logits, np.ndarray):
+            logits = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32))
+        self.x.copy_(x)
+        self.logits.copy_(logits)
+        torch.cuda.current_stream(self.dev).synchronize()   # inputs ready before the layer's streams run
+
+    def expert_block(self, e: int) -> torch.Tensor:
+        """The pool block of expert e (device or host tensor view)."""
+        n_local = self.cfg.n_local
+        return self._local_t[e] if e < n_local else self._remote_t[e - n_local]
+
+    # ------------------------------------------------------------------ steps
+    def route_permute(self) -> None:
+        cfg, cs = self.cfg, self.compute_stream
+        B.moe_route(self.logits, cfg.T, cfg.E, cfg.k, self.topk_idx, self.topk_w, self.status, cs)
+        B.moe_permute(self.topk_idx, cfg.T, cfg.E, cfg.k, self.x, cfg.H, self.dt, self.counts,
+                      self.offsets, self.row_of, self.src_of, self.x_perm, self.ws_perm,
+                      self.ws_perm_bytes, self.status, cs)
+
+    def routed_ids(self) -> Sequence[int]:
+        """Read counts back (one small copy and a sync) and return the expert set of the buffer:
+        every local expert plus the remote experts that received tokens, ascending."""
+        cfg, cs = self.cfg, self.compute_stream
+        with torch.cuda.stream(cs):
+            self.counts_host.copy_(self.counts, non_blocking=True)
+        cs.synchronize()
+        c = self.counts_host.numpy()
+        remote = np.nonzero(c[cfg.n_local:])[0] + cfg.n_local
+        return list(range(cfg.n_local)) + [int(e) for e in remote]
+
+    def fill_half(self, half: int, ids: Sequence[int], wait_free: bool = True) -> None:
+        """Copy stream: merge the local experts (and the slot map) and prefetch the remote ones."""
+        ws = self.free[half] if wait_free else None
+        B.moe_merge_weights(self.local_pool, ids, self.wbufs[half], self.copy_stream,
+                            wait_free=ws, ready=None, copy_mode=self.copy_mode)
+        B.moe_prefetch_layer(self.remote_pool, ids, self.wbufs[half], self.copy_stream,
+                             wait_free=None, ready=self.ready[half], copy_mode=self.copy_mode)
+        self.last_ids = list(ids)
+
+    def expert_compute(self, half: int, x_perm=None) -> None:
+        """Compute stream: wait for the half, grouped SwiGLU GEMM, combine, release the half."""
+        cfg, cs = self.cfg, self.compute_stream
+        B.moe_stream_wait_event(cs, self.ready[half])
+        B.moe_grouped_swiglu(self.x_perm if x_perm is None else x_perm, self.offsets, self.R, cfg.E,
+                             cfg.H, cfg.I, self.dt, self.wbufs[half], self.ws_gemm,
+                             self.ws_gemm_bytes, self.y_perm, self.status, cs)
+        B.moe_combine(self.y_perm, self.row_of, self.topk_w, cfg.T, cfg.k, cfg.H, self.y, cs)
+        B.moe_event_record(self.free[half], cs)
+
+    def forward(self, half: int = 0, remote: str = "routed") -> None:
+        """One whole layer step; remote = 'routed' (fetch only the remote experts that got
+        tokens, after a count read-back) or 'all' (fetch the whole remote share)."""
+        self.route_permute()
+        ids = self.routed_ids() if remote == "routed" else list(range(self.cfg.E))
+        self.fill_half(half, ids)
+        self.expert_compute(half)
+
+    def synchronize(self) -> None:
+        self.compute_stream.synchronize()
+        self.copy_stream.synchronize()
+
+    def read_status(self) -> int:
+        self.synchronize()
+        return int(self.status.item())
+
+    def outputs(self) -> Dict[str, np.ndarray]:
+        """Host copies of every output of the step (synchronises)."""
+        self.synchronize()
+        to = lambda t: t.detach().cpu()
+        x_perm = to(self.x_perm)
+        if x_perm.dtype == torch.bfloat16:
+            x_perm = x_perm.view(torch.int16).numpy().view(np.uint16)
+        else:
+            x_perm = x_perm.numpy()
+        return dict(idx=to(self.topk_idx).numpy(), w=to(self.topk_w).numpy(),
+                    counts=to(self.counts).numpy(), offsets=to(self.offsets).numpy(),
+                    row_of=to(self.row_of).numpy(), src_of=to(self.src_of).numpy(),
+                    x_perm=x_perm, y_perm=to(self.y_perm).numpy(), y=to(self.y).numpy(),
+                    status=int(self.status.item()))
+
+    def close(self) -> None:
+        for ev in self.ready + self.free:
+            B.moe_event_destroy(ev)
+        self.ready, self.free = [], []
+
+
+def block_to_numpy(block: torch.Tensor) -> np.ndarray:
+    """An expert block (torch, any device) as a host numpy array: float32, or uint16 bf16 bits."""
+    b = block.detach().cpu()
+    if b.dtype == torch.bfloat16:
+        return b.view(torch.int16).numpy().view(np.uint16)
+    return b.numpy()
