@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Throughput of the DWDP-style MoE layer forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input,
+with the weight pools and inputs already resident in HBM:
+
+    route -> permute (counts, offsets, permutation, row gather)
+    -> read the per-expert counts back (the routed remote set depends on them)
+    -> copy stream: merge the local experts into the merged buffer half and
+       prefetch the routed remote experts from the stand-in peer pool (SDMA)
+    -> compute stream waits for the copies -> grouped SwiGLU GEMM -> combine
+
+Steps alternate between the two halves of the double buffer.  The default
+workload is the DeepSeek-R1-shaped decode step (64 tokens, hidden 7168,
+256 experts with SwiGLU intermediate 2048, top-8, 64 local / 192 remote).
+
+Prints ONE JSON line: tokens/s of the whole step, the roofline of the
+dominant kernel (the grouped SwiGLU GEMM, timed with HIP events on its own
+stream inside the timed region), and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="r1_decode_t64")
+    p.add_argument("--remote", choices=["routed", "all"], default="routed",
+                   help="prefetch only the routed remote experts, or the whole remote share")
+    p.add_argument("--copy-mode", choices=["sdma", "any"], default="sdma")
+    p.add_argument("--cpu-sample-tokens", type=int, default=24)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(cfg, L, n_tokens):
+    """The oracle as it stands, on a bounded sample: routing and permutation of all tokens,
+    the layer output of n_tokens tokens (every expert they route to is decoded once)."""
+    import numpy as np
+    from oracle import moe as O
+    from grouped_gemm_weights_amd import synth
+    from grouped_gemm_weights_amd.layer import block_to_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    x = synth.activations(cfg)
+    logits = synth.logits(cfg)
+    tokens = list(range(min(n_tokens, cfg.T)))
+    # expert blocks are host copies taken before the clock starts (the oracle reads host memory)
+    idx, _ = O.route(logits[tokens], cfg.k)
+    blocks = {int(e): block_to_numpy(L.expert_block(int(e))) for e in np.unique(idx)}
+    t0 = time.perf_counter()
+    idx_all, w_all = O.route(logits, cfg.k)
+    counts = O.expert_counts(idx_all, cfg.E)
+    O.expert_offsets(counts)
+    O.permutation(idx_all, cfg.E)
+    O.moe_layer_tokens(x, logits, cfg.k, lambda e: blocks[e], cfg.H, cfg.I,
+                       round_h=cfg.dtype == "bf16", tokens=tokens)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(tokens) / dt, 4), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(tokens)} of {cfg.T} tokens through the float64 oracle "
+                      f"(routing and permutation of all {cfg.T} tokens included), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from grouped_gemm_weights_amd import binding as B
+    from grouped_gemm_weights_amd import synth
+    from grouped_gemm_weights_amd.layer import MoELayer
+
+    cfg = synth.config(args.config)
+    if cfg.layers != 1:
+        print("pipeline workloads are timed by bench_pipeline (not in this build yet)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copy_mode = B.MOE_COPY_SDMA if args.copy_mode == "sdma" else B.MOE_COPY_ANY
+    L = MoELayer(cfg, device=dev, copy_mode=copy_mode)
+    local = synth.pool_torch(cfg, 0, 0, cfg.n_local, dev)
+    remote = synth.pool_torch(cfg, 0, cfg.n_local, cfg.E - cfg.n_local, dev)
+    L.set_pools(local, remote)
+    L.set_inputs(synth.activations(cfg), synth.logits(cfg))
+    cs, ps = L.compute_stream, L.copy_stream
+
+    nev = args.steps
+    mk = lambda: [B.moe_event_create(True) for _ in range(nev)]
+    ev = {k: mk() for k in ("start", "rp_end", "gemm0", "gemm1", "end", "copy0", "copy1")}
+
+    def step(i, timed):
+        h = i % 2
+        if timed:
+            B.moe_event_record(ev["start"][i], cs)
+        L.route_permute()
+        if timed:
+            B.moe_event_record(ev["rp_end"][i], cs)
+        ids = L.routed_ids() if args.remote == "routed" else list(range(cfg.E))
+        if timed:
+            B.moe_event_record(ev["copy0"][i], ps)
+        L.fill_half(h, ids)
+        if timed:
+            B.moe_event_record(ev["copy1"][i], ps)
+        B.moe_stream_wait_event(cs, L.ready[h])
+        if timed:
+            B.moe_event_record(ev["gemm0"][i], cs)
+        B.moe_grouped_swiglu(L.x_perm, L.offsets, L.R, cfg.E, cfg.H, cfg.I, L.dt, L.wbufs[h],
+                             L.ws_gemm, L.ws_gemm_bytes, L.y_perm, L.status, cs)
+        if timed:
+            B.moe_event_record(ev["gemm1"][i], cs)
+        B.moe_combine(L.y_perm, L.row_of, L.topk_w, cfg.T, cfg.k, cfg.H, L.y, cs)
+        B.moe_event_record(L.free[h], cs)
+        if timed:
+            B.moe_event_record(ev["end"][i], cs)
+        return ids
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ids = step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert L.read_status() == 0, "device status set during the benchmark"
+
+    el = lambda a, b: float(np.mean([B.moe_event_elapsed_ms(ev[a][i], ev[b][i]) for i in range(nev)]))
+    gemm_ms = el("gemm0", "gemm1")
+    combine_ms = el("gemm1", "end")
+    rp_ms = el("start", "rp_end")
+    copy_ms = el("copy0", "copy1")
+    layer_ms = el("start", "end")
+
+    counts = L.counts.cpu().numpy()
+    n_active = int((counts > 0).sum())
+    eb = synth.expert_block_bytes(cfg)
+    R = cfg.T * cfg.k
+    alg_bytes = n_active * eb + R * cfg.H * 2 + R * cfg.H * 4       # weights read + x_perm + y_perm
+    alg_flop = 6.0 * cfg.H * cfg.I * R
+    copy_bytes = len(ids) * eb
+    gemm_gbps = alg_bytes / (gemm_ms * 1e-3) / 1e9
+    gemm_tflops = alg_flop / (gemm_ms * 1e-3) / 1e12
+    ai = alg_flop / alg_bytes
+    if ai < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        roof = {"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None}
+    roof.update({"kernel": "moe_grouped_swiglu (tile plan + gate/up GEMM + down GEMM)",
+                 "avg_ms": round(gemm_ms, 4), "alg_bytes": alg_bytes, "alg_flop": alg_flop})
+
+    result = {
+        "metric": "MoE layer tokens/s + grouped-GEMM % of HBM/MFMA roofline, R1 shape, 1 GPU",
+        "value": round(cfg.T * args.steps / wall, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
+                   "experts": cfg.E, "top_k": cfg.k, "local_experts": cfg.n_local,
+                   "remote_fetch": args.remote, "copy_engine": args.copy_mode,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "breakdown_ms": {"route_permute": round(rp_ms, 4), "merge_prefetch_copy": round(copy_ms, 4),
+                         "grouped_swiglu": round(gemm_ms, 4), "combine": round(combine_ms, 4),
+                         "layer_events": round(layer_ms, 4)},
+        "copy": {"bytes": copy_bytes, "experts": len(ids), "GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1)},
+        "active_experts": n_active,
+        "gemm_TFLOPs": round(gemm_tflops, 2),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -288,13 +288,237 @@ struct GemmShape {
   }
 };
 
+
+// ---------------------------------------------------------------------------
+// Prefill tile GEMM: 256 x 256 block tile, 8 waves (two per SIMD), 32x32x16
+// MFMA, BK = 64, LDS double buffer (144 KB of the CU's 160 KB).
+//
+// DUAL (gate/up): the B tile holds 128 Wg rows and the same 128 Wu rows, so
+// a block produces 256 rows x 128 columns of h; each wave owns 128 rows x 32
+// columns of both g and u and applies silu(g) * u in registers.  !DUAL: the B
+// tile is 256 rows of one matrix; each wave owns 128 rows x 64 columns.
+//
+// Work order: the (m-tile, n-tile) items are cut into 8 contiguous chunks,
+// one per XCD (workgroup i runs on XCD i % 8), and inside a chunk groups of
+// kMGroup consecutive m-tiles sweep the n-tiles together, so the blocks that
+// run at the same time on one XCD share A tiles and weight panels in its L2.
+// ---------------------------------------------------------------------------
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kXcds = 8;
+constexpr int kMGroup = 4;
+
+template <bool DUAL, bool OUT_BF16>
+__global__ __launch_bounds__(512) void gemm_big_kernel(
+    const uint16_t* __restrict__ A, int lda, const char* __restrict__ wbase, int64_t expert_bytes,
+    int64_t b0_off, int64_t b1_off, int N, int K, const Tile* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles, int dense_M, void* __restrict__ out, int ldo) {
+  constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+  constexpr int LDS_LD = BK + 8;
+  constexpr int KC = BK / 8;
+  constexpr int CA = BM * KC / NT;   // 4
+  constexpr int CB = BN * KC / NT;   // 4
+  constexpr int OUTN = DUAL ? BN / 2 : BN;
+
+  const int n_m = tiles ? *n_tiles : (dense_M + BM - 1) / BM;
+  const int n_n = (N + OUTN - 1) / OUTN;
+  const int total = n_m * n_n;
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int local = blockIdx.x / kXcds;
+  if (local >= chunk) return;
+  const int w = (blockIdx.x % kXcds) * chunk + local;
+  if (w >= total) return;
+  const int g = w / (n_n * kMGroup);
+  const int gsize = min(kMGroup, n_m - g * kMGroup);
+  const int rem = w - g * (n_n * kMGroup);
+  const int nt = rem / gsize;
+  const int mt = g * kMGroup + rem % gsize;
+
+  Tile tile;
+  if (tiles) {
+    tile = tiles[mt];
+  } else {
+    tile.expert = 0;
+    tile.row0 = mt * BM;
+    tile.rows = min(BM, dense_M - tile.row0);
+    tile.slot = 0;
+  }
+  const int n0 = nt * OUTN;
+
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* As = smem;                       // [2][BM][LDS_LD]
+  uint16_t* Bs = smem + 2 * BM * LDS_LD;     // [2][BN][LDS_LD]
+
+  const char* wexp = wbase + static_cast<int64_t>(tile.slot) * expert_bytes;
+  const uint16_t* B0 = reinterpret_cast<const uint16_t*>(wexp + b0_off);
+  const uint16_t* B1 = reinterpret_cast<const uint16_t*>(wexp + b1_off);
+  const uint16_t* Arow = A + static_cast<int64_t>(tile.row0) * lda;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm0 = (wave >> 2) * 128;          // 2 waves down M
+  const int wq = wave & 3;                     // 4 waves across N
+
+  // per-thread load slots (fixed over the K loop)
+  const uint16_t* a_src[CA];
+  bool a_ok[CA];
+  int a_lds[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int c = tid + i * NT;
+    const int r = c / KC, kc = c % KC;
+    a_ok[i] = r < tile.rows;
+    a_src[i] = Arow + static_cast<int64_t>(a_ok[i] ? r : 0) * lda + kc * 8;
+    a_lds[i] = r * LDS_LD + kc * 8;
+  }
+  const uint16_t* b_src[CB];
+  bool b_ok[CB];
+  int b_lds[CB];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int c = tid + i * NT;
+    const int r = c / KC, kc = c % KC;
+    const int n = n0 + (DUAL ? (r & (BN / 2 - 1)) : r);
+    const uint16_t* Bm = (DUAL && r >= BN / 2) ? B1 : B0;
+    b_ok[i] = n < N;
+    b_src[i] = Bm + static_cast<int64_t>(b_ok[i] ? n : 0) * K + kc * 8;
+    b_lds[i] = r * LDS_LD + kc * 8;
+  }
+
+  uint4 ra[CA], rb[CB];
+#define BIG_LOAD(k0)                                                              \
+  do {                                                                            \
+    _Pragma("unroll") for (int i = 0; i < CA; ++i) {                              \
+      ra[i] = make_uint4(0, 0, 0, 0);                                             \
+      if (a_ok[i] && (k0) + (((tid + i * NT) % KC) * 8) < K)                      \
+        ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + (k0));                 \
+    }                                                                             \
+    _Pragma("unroll") for (int i = 0; i < CB; ++i) {                              \
+      rb[i] = make_uint4(0, 0, 0, 0);                                             \
+      if (b_ok[i] && (k0) + (((tid + i * NT) % KC) * 8) < K)                      \
+        rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + (k0));                 \
+    }                                                                             \
+  } while (0)
+#define BIG_STORE(buf)                                                            \
+  do {                                                                            \
+    _Pragma("unroll") for (int i = 0; i < CA; ++i)                                \
+      *reinterpret_cast<uint4*>(As + (buf) * BM * LDS_LD + a_lds[i]) = ra[i];     \
+    _Pragma("unroll") for (int i = 0; i < CB; ++i)                                \
+      *reinterpret_cast<uint4*>(Bs + (buf) * BN * LDS_LD + b_lds[i]) = rb[i];     \
+  } while (0)
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // operand rows of this lane inside the LDS tiles
+  const int lrow = lane & 31;
+  const int lk = (lane >> 5) * 8;
+  int brow[2];
+  if (DUAL) {
+    brow[0] = wq * 32 + lrow;
+    brow[1] = BN / 2 + wq * 32 + lrow;
+  } else {
+    brow[0] = wq * 64 + lrow;
+    brow[1] = wq * 64 + 32 + lrow;
+  }
+
+  const int nk = (K + BK - 1) / BK;
+  BIG_LOAD(0);
+  BIG_STORE(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) BIG_LOAD((kt + 1) * BK);
+    const uint16_t* as = As + cur * BM * LDS_LD;
+    const uint16_t* bs = Bs + cur * BN * LDS_LD;
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 16) {
+      bf16x8_t a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(as + (wm0 + i * 32 + lrow) * LDS_LD + ks + lk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(bs + brow[j] * LDS_LD + ks + lk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) BIG_STORE(cur ^ 1);
+    __syncthreads();
+  }
+#undef BIG_LOAD
+#undef BIG_STORE
+
+  // epilogue: element q of a 32x32 block sits at row (q/4)*8 + (lane/32)*4 + q%4, column lane%32
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = wm0 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+      if (r >= tile.rows) continue;
+      const int64_t orow = static_cast<int64_t>(tile.row0 + r) * ldo;
+      if (DUAL) {
+        const int n = n0 + wq * 32 + lrow;
+        if (n < N)
+          static_cast<uint16_t*>(out)[orow + n] = f32_to_bf16(silu_f32(acc[i][0][q]) * acc[i][1][q]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + wq * 64 + j * 32 + lrow;
+          if (n >= N) continue;
+          if (OUT_BF16) static_cast<uint16_t*>(out)[orow + n] = f32_to_bf16(acc[i][j][q]);
+          else static_cast<float*>(out)[orow + n] = acc[i][j][q];
+        }
+      }
+    }
+}
+
+template <bool DUAL, bool OUT_BF16>
+struct GemmBig {
+  static constexpr int BM = 256;
+  static constexpr size_t kLds = 2 * static_cast<size_t>(256 + 256) * (64 + 8) * sizeof(uint16_t);
+
+  // grid_m: upper bound on the number of m-tiles
+  static int launch(const uint16_t* A, int lda, const char* wbase, int64_t expert_bytes,
+                    int64_t b0_off, int64_t b1_off, int N, int K, const Tile* tiles,
+                    const int32_t* n_tiles, int64_t grid_m, int dense_M, void* out, int ldo,
+                    hipStream_t s) {
+    auto kern = gemm_big_kernel<DUAL, OUT_BF16>;
+    static bool configured = false;
+    if (!configured) {
+      MOE_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        static_cast<int>(kLds)));
+      configured = true;
+    }
+    if (grid_m <= 0) return MOE_OK;
+    const int outn = DUAL ? 128 : 256;
+    const int64_t items = grid_m * ceil_div(N, outn);
+    const int64_t blocks = ceil_div64(items, kXcds) * kXcds;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(512), kLds, s, A, lda, wbase,
+                       expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles, dense_M, out, ldo);
+    MOE_LAUNCH_CHECK("gemm_big_kernel launch");
+    return MOE_OK;
+  }
+};
+
 // decode shapes: 16-row tiles, weights streamed in 128-deep K steps
 using Gemm1Decode = GemmShape<16, 64, 128, 1, 4, true, false>;
 using Gemm2Decode = GemmShape<16, 64, 128, 1, 4, false, false>;
 // prefill shapes: 128-row tiles
-using Gemm1Prefill = GemmShape<128, 64, 64, 2, 2, true, false>;
-using Gemm2Prefill = GemmShape<128, 128, 64, 2, 2, false, false>;
-using DenseBf16 = GemmShape<128, 128, 64, 2, 2, false, true>;
+using Gemm1Prefill = GemmBig<true, false>;
+using Gemm2Prefill = GemmBig<false, false>;
+using DenseBf16 = GemmBig<false, true>;
 
 // ---------------------------------------------------------------------------
 // f32 path
@@ -415,7 +639,7 @@ extern "C" int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, in
   Tile* tiles = reinterpret_cast<Tile*>(wsb + L.tiles_off);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(wsb + L.count_off);
   const bool decode = static_cast<int64_t>(R) <= 4 * static_cast<int64_t>(E);
-  const int BM = decode ? 16 : 128;
+  const int BM = decode ? 16 : GemmBig<true, false>::BM;
   const int64_t grid_tiles = ceil_div64(R, BM) + std::min(E, R);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(MOE_MAX_E), 0, s, offsets, E, BM, w->slot_of, tiles,
                      n_tiles, status);
@@ -446,5 +670,6 @@ extern "C" int moe_dense_gemm(const void* x, const void* w, int M, int N, int K,
   if (M == 0) return MOE_OK;
   if (!x || !w || !out) return fail(MOE_ERR_ARG, "moe_dense_gemm: null pointer");
   return DenseBf16::launch(static_cast<const uint16_t*>(x), K, static_cast<const char*>(w), 0, 0, 0,
-                           N, K, nullptr, nullptr, ceil_div(M, 128), M, out, N, as_stream(stream));
+                           N, K, nullptr, nullptr, ceil_div(M, DenseBf16::BM), M, out, N,
+                           as_stream(stream));
 }
