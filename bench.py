@@ -79,6 +79,79 @@ def cpu_baseline(cfg, L, n_tokens):
                       f"(routing and permutation of all {cfg.T} tokens included), {dt:.1f} s"}
 
 
+def bench_pipeline(args, cfg, dev, copy_mode):
+    """The multi-layer pipeline: prefetch of layer l+1 on the copy stream hidden behind layer
+    l's MoE block and layer l+1's dense stand-in block; hidden fraction and per-layer latency."""
+    import numpy as np
+    import torch
+    from grouped_gemm_weights_amd import binding as B
+    from grouped_gemm_weights_amd import synth
+    from grouped_gemm_weights_amd.pipeline import MoEPipeline
+
+    P = MoEPipeline(cfg, device=dev, copy_mode=copy_mode)
+    n = cfg.layers
+    keys = ("c0", "c1", "wait0", "wait1", "d0", "m1", "g1")
+    mk = lambda: {k: [B.moe_event_create(True) for _ in range(n)] for k in keys}
+    for _ in range(args.warmup):
+        P.forward()
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        P.forward(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert P.L.read_status() == 0, "device status set during the benchmark"
+    el = B.moe_event_elapsed_ms
+    P_l, stall, Lat, comp_pipe, gemm = [], [], [], [], []
+    for ev in evs:
+        for l in range(n):
+            P_l.append(el(ev["c0"][l], ev["c1"][l]))
+            stall.append(el(ev["wait0"][l], ev["wait1"][l]))
+            comp_pipe.append(el(ev["d0"][l], ev["m1"][l]) - stall[-1])
+            gemm.append(el(ev["wait1"][l], ev["g1"][l]))
+            if l > 0:
+                Lat.append(el(ev["m1"][l - 1], ev["m1"][l]))
+    sev = mk()
+    P.forward_serial(sev)
+    torch.cuda.synchronize()
+    C_alone = [el(sev["d0"][l], sev["m1"][l]) for l in range(n)]
+    P_alone = [el(sev["c0"][l], sev["c1"][l]) for l in range(n)]
+    mean = lambda v: float(np.mean(v))
+    H = 1.0 - sum(stall) / sum(P_l)
+    eb = synth.expert_block_bytes(cfg)
+    R = cfg.T * cfg.k
+    gemm_ms = mean(gemm)
+    alg_bytes = cfg.E * eb + R * cfg.H * 6
+    alg_flop = 6.0 * cfg.H * cfg.I * R
+    gbps = alg_bytes / (gemm_ms * 1e-3) / 1e9
+    return {
+        "metric": "MoE layer tokens/s + grouped-GEMM % of HBM/MFMA roofline, R1 shape, 1 GPU",
+        "value": round(cfg.T * args.steps / wall, 2), "unit": "tokens/s (through all layers)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": n, "tokens": cfg.T, "hidden": cfg.H,
+                   "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k,
+                   "local_experts": cfg.n_local, "copy_engine": args.copy_mode,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "moe_grouped_swiglu, pipelined layers (with the copy running)",
+                     "avg_ms": round(gemm_ms, 4), "alg_bytes": alg_bytes, "alg_flop": alg_flop,
+                     "TFLOPs": round(alg_flop / (gemm_ms * 1e-3) / 1e12, 1)},
+        "pipeline": {
+            "prefetch_ms": round(mean(P_l), 3), "prefetch_alone_ms": round(mean(P_alone), 3),
+            "copy_GBps": round(cfg.E * eb / (mean(P_l) * 1e-3) / 1e9, 1),
+            "stall_ms": round(mean(stall), 3), "hidden_fraction": round(H, 4),
+            "compute_pipelined_ms": round(mean(comp_pipe), 3), "compute_alone_ms": round(mean(C_alone), 3),
+            "contention_slowdown": round(mean(comp_pipe) / mean(C_alone), 3),
+            "layer_latency_ms": round(mean(Lat), 3),
+            "max_compute_prefetch_ms": round(max(mean(C_alone), mean(P_alone)), 3),
+        },
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -93,12 +166,12 @@ def main():
     from grouped_gemm_weights_amd.layer import MoELayer
 
     cfg = synth.config(args.config)
-    if cfg.layers != 1:
-        print("pipeline workloads are timed by bench_pipeline (not in this build yet)", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     copy_mode = B.MOE_COPY_SDMA if args.copy_mode == "sdma" else B.MOE_COPY_ANY
+    if cfg.layers != 1:
+        print(json.dumps(bench_pipeline(args, cfg, dev, copy_mode)), flush=True)
+        return
     L = MoELayer(cfg, device=dev, copy_mode=copy_mode)
     local = synth.pool_torch(cfg, 0, 0, cfg.n_local, dev)
     remote = synth.pool_torch(cfg, 0, cfg.n_local, cfg.E - cfg.n_local, dev)

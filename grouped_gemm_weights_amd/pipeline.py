@@ -1,0 +1,149 @@
+"""Multi-layer MoE pipeline with the copy-stream prefetch one layer ahead.
+
+The schedule is the one of the DWDP explainer's prefetch-schedule panel:
+while the compute stream runs layer l's MoE block and layer l+1's attention
+block (here a dense bf16 GEMM stands in for attention), the copy stream fills
+the alternate half of the merged buffer with layer l+1's experts: the merge
+copies the local experts and the prefetch pulls the whole remote share (the
+routing of layer l+1 is not known yet).  Per layer on the compute stream:
+
+    A_l = bf16(x_l W_l^T)                          moe_dense_gemm
+    wait(ready[l % 2])                             <- the layer's experts are in place
+    route -> permute -> grouped SwiGLU -> combine  on half l % 2
+    free[l % 2]                                    -> the half may be refilled
+    x_{l+1} = bf16(x_l + y_l)                      moe_residual_add
+
+and on the copy stream: wait(free[(l+1) % 2]) -> merge + prefetch of layer
+l+1 into half (l+1) % 2 -> ready[(l+1) % 2].  Per-layer latency is then
+max(compute, prefetch) (explainer, per-layer latency panel).
+
+Every step runs in the library (C ABI); this module only orders the calls
+and records events.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+from . import synth
+from .layer import MoELayer
+
+
+class MoEPipeline:
+    def __init__(self, cfg: synth.MoEConfig, device="cuda", copy_mode: int = B.MOE_COPY_SDMA):
+        assert cfg.dtype == "bf16", "the pipeline runs the bf16 workloads"
+        self.cfg = cfg
+        self.dev = torch.device(device)
+        self.L = MoELayer(cfg, device=self.dev, copy_mode=copy_mode)
+        L = self.L
+        self.n = cfg.layers
+        self.locals: List[torch.Tensor] = []
+        self.remotes: List[torch.Tensor] = []
+        self.local_pools, self.remote_pools = [], []
+        self.logits: List[torch.Tensor] = []
+        self.w_attn: List[torch.Tensor] = []
+        for l in range(self.n):
+            loc = synth.pool_torch(cfg, l, 0, cfg.n_local, self.dev)
+            rem = synth.pool_torch(cfg, l, cfg.n_local, cfg.E - cfg.n_local, self.dev)
+            self.locals.append(loc)
+            self.remotes.append(rem)
+            self.local_pools.append(B.pool(loc, L.eb, 0, cfg.n_local))
+            self.remote_pools.append(B.pool(rem, L.eb, cfg.n_local, cfg.E - cfg.n_local))
+            self.logits.append(torch.from_numpy(synth.logits(cfg, l)).to(self.dev))
+            self.w_attn.append(synth.dense_weight_torch(cfg, l, self.dev))
+        x0 = synth.activations(cfg, 0)
+        self.x0 = torch.from_numpy(x0.view(np.int16)).view(torch.bfloat16).to(self.dev)
+        self.x = torch.empty_like(self.x0)
+        self.a = torch.empty_like(self.x0)
+        self.all_ids = list(range(cfg.E))
+        torch.cuda.current_stream(self.dev).synchronize()
+
+    # -------------------------------------------------------------- pieces
+    def fill(self, l: int, wait_free: bool = True, ev: Optional[Dict[str, list]] = None) -> None:
+        """Copy stream: wait until half l % 2 is free, then merge layer l's local experts and
+        prefetch its remote share into it; ``ev`` c0/c1 bracket the copies themselves."""
+        L, h = self.L, l % 2
+        if wait_free:
+            B.moe_stream_wait_event(L.copy_stream, L.free[h])
+        if ev is not None:
+            B.moe_event_record(ev["c0"][l], L.copy_stream)
+        B.moe_merge_weights(self.local_pools[l], self.all_ids, L.wbufs[h], L.copy_stream,
+                            wait_free=None, ready=None, copy_mode=L.copy_mode)
+        B.moe_prefetch_layer(self.remote_pools[l], self.all_ids, L.wbufs[h], L.copy_stream,
+                             wait_free=None, ready=L.ready[h], copy_mode=L.copy_mode)
+        if ev is not None:
+            B.moe_event_record(ev["c1"][l], L.copy_stream)
+
+    def dense(self, l: int) -> None:
+        cfg = self.cfg
+        B.moe_dense_gemm(self.x, self.w_attn[l], cfg.T, cfg.H, cfg.H, self.a, self.L.compute_stream)
+
+    def moe(self, l: int, ev: Optional[Dict[str, list]] = None) -> None:
+        """Route -> permute -> (wait for the half) -> grouped SwiGLU -> combine for layer l."""
+        L, cfg, cs, h = self.L, self.cfg, self.L.compute_stream, l % 2
+        L.logits, L.x = self.logits[l], self.a
+        L.route_permute()
+        if ev is not None:
+            B.moe_event_record(ev["wait0"][l], cs)
+        B.moe_stream_wait_event(cs, L.ready[h])
+        if ev is not None:
+            B.moe_event_record(ev["wait1"][l], cs)
+        B.moe_grouped_swiglu(L.x_perm, L.offsets, L.R, cfg.E, cfg.H, cfg.I, L.dt, L.wbufs[h],
+                             L.ws_gemm, L.ws_gemm_bytes, L.y_perm, L.status, cs)
+        if ev is not None and "g1" in ev:
+            B.moe_event_record(ev["g1"][l], cs)
+        B.moe_combine(L.y_perm, L.row_of, L.topk_w, cfg.T, cfg.k, cfg.H, L.y, cs)
+        B.moe_event_record(L.free[h], cs)
+
+    def residual(self) -> None:
+        cfg = self.cfg
+        B.moe_residual_add(self.x, self.L.y, cfg.T * cfg.H, self.x, self.L.compute_stream)
+
+    # -------------------------------------------------------------- runs
+    def reset(self) -> None:
+        with torch.cuda.stream(self.L.compute_stream):
+            self.x.copy_(self.x0)
+
+    def forward(self, ev: Optional[Dict[str, list]] = None, layer_hook=None) -> None:
+        """The pipelined pass over all layers.  ``ev`` (optional) holds per-layer timing events:
+        c0/c1 around each fill on the copy stream, wait0/wait1 around the wait for the half,
+        d0 at the start of the dense block and m1 at the end of each MoE block."""
+        L, cs, ps = self.L, self.L.compute_stream, self.L.copy_stream
+        self.reset()
+        self.fill(0, wait_free=True, ev=ev)
+        for l in range(self.n):
+            if ev is not None:
+                B.moe_event_record(ev["d0"][l], cs)
+            self.dense(l)
+            if l + 1 < self.n:
+                self.fill(l + 1, wait_free=True, ev=ev)
+            self.moe(l, ev)
+            if ev is not None:
+                B.moe_event_record(ev["m1"][l], cs)
+            if layer_hook is not None:
+                layer_hook(l)
+            self.residual()
+
+    def forward_serial(self, ev: Optional[Dict[str, list]] = None) -> None:
+        """Each layer's copies finish before its compute starts (no overlap): the compute
+        time alone, for the contention-slowdown figure."""
+        L, cs, ps = self.L, self.L.compute_stream, self.L.copy_stream
+        self.reset()
+        for l in range(self.n):
+            self.fill(l, wait_free=True, ev=ev)
+            ps.synchronize()
+            cs.synchronize()
+            if ev is not None:
+                B.moe_event_record(ev["d0"][l], cs)
+            self.dense(l)
+            self.moe(l)
+            if ev is not None:
+                B.moe_event_record(ev["m1"][l], cs)
+            self.residual()
+        cs.synchronize()
+
+    def synchronize(self) -> None:
+        self.L.synchronize()

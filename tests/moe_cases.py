@@ -76,6 +76,25 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref))) / max(rms, 1e-300)
 
 
+def bf16_ulp(v) -> np.ndarray:
+    """Spacing of bf16 values at |v| (2**(e-8) for |v| in [2**(e-1), 2**e); 2**-133 below 2**-126)."""
+    _, e = np.frexp(np.asarray(v, dtype=np.float64))
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def rel_err_bf16(got, ref, roundings: int = 1) -> float:
+    """rel_err for outputs stored in bf16: both sides round to bf16 once at the end, so an
+    element may differ by one bf16 spacing of the reference when the exact values fall on
+    opposite sides of a rounding boundary; only the excess over that spacing counts.  A value
+    re-rounded to bf16 at each of several stages may cross one boundary per stage
+    (``roundings`` spacings)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    excess = np.maximum(np.abs(got - ref) - roundings * bf16_ulp(ref), 0.0)
+    return float(np.max(excess)) / max(rms, 1e-300)
+
+
 def check_routing(cfg, out, logits):
     """Bit-exact ids / counts / offsets / permutation and weights within W_TOL, on all tokens."""
     idx, w = O.route(logits, cfg.k)
