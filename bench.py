@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--copy-mode", choices=["sdma", "any"], default="sdma")
     p.add_argument("--cpu-sample-tokens", type=int, default=24)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate", action="store_true",
+                   help="run only a plain streaming kernel of known size (moe_residual_add over "
+                        "1 GiB elements), the reference for scaling the HBM byte counters")
     return p.parse_args()
 
 
@@ -152,8 +155,43 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     }
 
 
+def calibrate():
+    """A plain streaming kernel with known traffic: out = bf16(x + y) over n elements reads
+    2n + 4n bytes and writes 2n bytes."""
+    import torch
+    from grouped_gemm_weights_amd import binding as B
+    n = 1 << 30
+    dev = torch.device("cuda:0")
+    x = torch.zeros(n, dtype=torch.bfloat16, device=dev)
+    y = torch.zeros(n, dtype=torch.float32, device=dev)
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        B.moe_residual_add(x, y, n, out, None)
+    torch.cuda.synchronize()
+    return {"kernel": "residual_kernel", "launches": 3, "read_bytes_per_launch": 6 * n,
+            "write_bytes_per_launch": 2 * n}
+
+
+def traffic_from_profiles(kernel_file):
+    """HBM bytes per moe_grouped_swiglu call measured with rocprofv3 counters, if they were taken
+    on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "grouped_swiglu_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(kernel_file, "rb").read()
+    if rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec
+
+
 def main():
     args = parse()
+    if args.calibrate:
+        print(json.dumps(calibrate()), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -245,6 +283,11 @@ def main():
                 "traffic": None}
     roof.update({"kernel": "moe_grouped_swiglu (tile plan + gate/up GEMM + down GEMM)",
                  "avg_ms": round(gemm_ms, 4), "alg_bytes": alg_bytes, "alg_flop": alg_flop})
+    tr = traffic_from_profiles(os.path.join(ROOT, "grouped_gemm_weights_amd", "csrc", "grouped_swiglu.hip"))
+    if tr is not None and tr.get("workload") == cfg.name:
+        roof["traffic"] = tr["hbm_bytes_per_call"]
+        roof["traffic_detail"] = {"read": tr["read_bytes_per_call"], "write": tr["write_bytes_per_call"],
+                                  "source": "profiles/grouped_swiglu_traffic.json"}
 
     result = {
         "metric": "MoE layer tokens/s + grouped-GEMM % of HBM/MFMA roofline, R1 shape, 1 GPU",
