@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--remote", choices=["routed", "all"], default="routed",
                    help="prefetch only the routed remote experts, or the whole remote share")
     p.add_argument("--copy-mode", choices=["sdma", "any"], default="sdma")
+    p.add_argument("--merge", choices=["copy", "stitched"], default="stitched",
+                   help="copy the local experts into each merged half, or stitch the local "
+                        "block into the half's virtual range so the merge copies nothing")
     p.add_argument("--cpu-sample-tokens", type=int, default=24)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate", action="store_true",
@@ -91,7 +94,7 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     from grouped_gemm_weights_amd import synth
     from grouped_gemm_weights_amd.pipeline import MoEPipeline
 
-    P = MoEPipeline(cfg, device=dev, copy_mode=copy_mode)
+    P = MoEPipeline(cfg, device=dev, copy_mode=copy_mode, stitched=args.merge == "stitched")
     n = cfg.layers
     keys = ("c0", "c1", "wait0", "wait1", "d0", "m1", "g1")
     mk = lambda: {k: [B.moe_event_create(True) for _ in range(n)] for k in keys}
@@ -119,6 +122,7 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     P.forward_serial(sev)
     torch.cuda.synchronize()
     C_alone = [el(sev["d0"][l], sev["m1"][l]) for l in range(n)]
+    P.close()
     P_alone = [el(sev["c0"][l], sev["c1"][l]) for l in range(n)]
     mean = lambda v: float(np.mean(v))
     H = 1.0 - sum(stall) / sum(P_l)
@@ -137,7 +141,7 @@ def bench_pipeline(args, cfg, dev, copy_mode):
         "config": {"workload": cfg.name, "layers": n, "tokens": cfg.T, "hidden": cfg.H,
                    "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k,
                    "local_experts": cfg.n_local, "copy_engine": args.copy_mode,
-                   "parallelism": "none (1 GPU)"},
+                   "merge": args.merge, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "moe_grouped_swiglu, pipelined layers (with the copy running)",
@@ -145,7 +149,8 @@ def bench_pipeline(args, cfg, dev, copy_mode):
                      "TFLOPs": round(alg_flop / (gemm_ms * 1e-3) / 1e12, 1)},
         "pipeline": {
             "prefetch_ms": round(mean(P_l), 3), "prefetch_alone_ms": round(mean(P_alone), 3),
-            "copy_GBps": round(cfg.E * eb / (mean(P_l) * 1e-3) / 1e9, 1),
+            "copy_bytes": (cfg.E - (cfg.n_local if P.stitched else 0)) * eb,
+            "copy_GBps": round((cfg.E - (cfg.n_local if P.stitched else 0)) * eb / (mean(P_l) * 1e-3) / 1e9, 1),
             "stall_ms": round(mean(stall), 3), "hidden_fraction": round(H, 4),
             "compute_pipelined_ms": round(mean(comp_pipe), 3), "compute_alone_ms": round(mean(C_alone), 3),
             "contention_slowdown": round(mean(comp_pipe) / mean(C_alone), 3),
@@ -210,7 +215,7 @@ def main():
     if cfg.layers != 1:
         print(json.dumps(bench_pipeline(args, cfg, dev, copy_mode)), flush=True)
         return
-    L = MoELayer(cfg, device=dev, copy_mode=copy_mode)
+    L = MoELayer(cfg, device=dev, copy_mode=copy_mode, stitched=args.merge == "stitched")
     local = synth.pool_torch(cfg, 0, 0, cfg.n_local, dev)
     remote = synth.pool_torch(cfg, 0, cfg.n_local, cfg.E - cfg.n_local, dev)
     L.set_pools(local, remote)
@@ -270,7 +275,7 @@ def main():
     R = cfg.T * cfg.k
     alg_bytes = n_active * eb + R * cfg.H * 2 + R * cfg.H * 4       # weights read + x_perm + y_perm
     alg_flop = 6.0 * cfg.H * cfg.I * R
-    copy_bytes = len(ids) * eb
+    copy_bytes = (len(ids) - (cfg.n_local if args.merge == "stitched" else 0)) * eb
     gemm_gbps = alg_bytes / (gemm_ms * 1e-3) / 1e9
     gemm_tflops = alg_flop / (gemm_ms * 1e-3) / 1e12
     ai = alg_flop / alg_bytes
@@ -305,7 +310,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.k, "local_experts": cfg.n_local,
                    "remote_fetch": args.remote, "copy_engine": args.copy_mode,
-                   "parallelism": "none (1 GPU)"},
+                   "merge": args.merge, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "breakdown_ms": {"route_permute": round(rp_ms, 4), "merge_prefetch_copy": round(copy_ms, 4),
                          "grouped_swiglu": round(gemm_ms, 4), "combine": round(combine_ms, 4),
@@ -316,6 +321,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_sample_tokens)
+    L.close()
     print(json.dumps(result), flush=True)
 
 

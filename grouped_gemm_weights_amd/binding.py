@@ -26,7 +26,8 @@ EXPORTS = (
     "moe_prefetch_layer", "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu",
     "moe_combine", "moe_dense_gemm", "moe_residual_add", "moe_event_create",
     "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms", "moe_stream_wait_event",
-    "moe_last_error", "moe_version",
+    "moe_last_error", "moe_version", "moe_vmm_granularity", "moe_vmm_create", "moe_vmm_map",
+    "moe_vmm_unmap", "moe_vmm_release",
 )
 
 
@@ -69,6 +70,11 @@ def _load() -> ctypes.CDLL:
         "moe_event_record": [P, P],
         "moe_event_elapsed_ms": [P, P, ctypes.POINTER(ctypes.c_float)],
         "moe_stream_wait_event": [P, P],
+        "moe_vmm_granularity": [I, PSZ],
+        "moe_vmm_create": [I, SZ, ctypes.POINTER(ctypes.c_void_p)],
+        "moe_vmm_map": [I, ctypes.POINTER(ctypes.c_void_p), PSZ, I, ctypes.POINTER(ctypes.c_void_p)],
+        "moe_vmm_unmap": [P, PSZ, I],
+        "moe_vmm_release": [P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -211,6 +217,37 @@ def moe_event_elapsed_ms(start, stop) -> float:
 
 def moe_stream_wait_event(stream, ev) -> None:
     _check("moe_stream_wait_event", lib.moe_stream_wait_event(stream_handle(stream), ev))
+
+
+def moe_vmm_granularity(device: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_vmm_granularity", lib.moe_vmm_granularity(device, ctypes.byref(n)))
+    return n.value
+
+
+def moe_vmm_create(nbytes: int, device: int = 0) -> int:
+    h = ctypes.c_void_p(0)
+    _check("moe_vmm_create", lib.moe_vmm_create(device, nbytes, ctypes.byref(h)))
+    return h.value
+
+
+def moe_vmm_map(phys: Sequence[int], sizes: Sequence[int], device: int = 0) -> int:
+    n = len(phys)
+    ph = (ctypes.c_void_p * n)(*phys)
+    sz = (ctypes.c_size_t * n)(*sizes)
+    va = ctypes.c_void_p(0)
+    _check("moe_vmm_map", lib.moe_vmm_map(device, ph, sz, n, ctypes.byref(va)))
+    return va.value
+
+
+def moe_vmm_unmap(va: int, sizes: Sequence[int]) -> None:
+    n = len(sizes)
+    sz = (ctypes.c_size_t * n)(*sizes)
+    _check("moe_vmm_unmap", lib.moe_vmm_unmap(va, sz, n))
+
+
+def moe_vmm_release(phys: int) -> None:
+    _check("moe_vmm_release", lib.moe_vmm_release(phys))
 
 
 def moe_last_error() -> str:

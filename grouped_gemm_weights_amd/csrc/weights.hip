@@ -99,7 +99,8 @@ int copy_pool_experts(const moe_pool* p, const int32_t* ids, int n, moe_wbuf* ds
     while (j < n && in_pool(ids[j]) && ids[j] == ids[j - 1] + 1) ++j;
     const char* src = static_cast<const char*>(p->base) + (ids[i] - lo) * eb;
     char* to = static_cast<char*>(dst->base) + static_cast<int64_t>(i) * eb;
-    MOE_HIP_CHECK(hipMemcpyAsync(to, src, static_cast<size_t>(j - i) * eb, kind, s));
+    // a run already in place (the local block stitched at the head of the range) needs no copy
+    if (src != to) MOE_HIP_CHECK(hipMemcpyAsync(to, src, static_cast<size_t>(j - i) * eb, kind, s));
     i = j;
   }
   return MOE_OK;

@@ -44,8 +44,13 @@ class MoELayer:
 
     def __init__(self, cfg: MoEConfig, device="cuda", n_slots: Optional[int] = None,
                  n_halves: int = 2, compute_stream=None, copy_stream=None,
-                 copy_mode: int = B.MOE_COPY_SDMA):
+                 copy_mode: int = B.MOE_COPY_SDMA, stitched: bool = False,
+                 allocate_halves: bool = True):
+        """stitched: each half is one virtual range over [the local-expert block | the half's own
+        block], so merging the local experts copies nothing (page stitching, moe_vmm_*).
+        allocate_halves=False leaves the halves to the caller (the pipeline builds per-layer ranges)."""
         self.cfg = cfg
+        self.stitched = stitched
         self.dev = torch.device(device)
         self.copy_mode = copy_mode
         T, E, k, H, I = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I
@@ -76,11 +81,28 @@ class MoELayer:
         self.n_slots = E if n_slots is None else n_slots
         self.halves = []
         self.wbufs = []
-        for _ in range(n_halves):
-            base = torch.empty((self.n_slots, self.eb), dtype=torch.uint8, device=d)
-            slot_of = torch.full((E,), -1, **i32)
-            self.halves.append((base, slot_of))
-            self.wbufs.append(B.wbuf(base, self.eb, self.n_slots, E, slot_of))
+        self.slot_maps = [torch.full((E,), -1, **i32) for _ in range(n_halves)]
+        self._vmm_ranges, self._vmm_phys = [], []
+        self.stitched_local_pools = []
+        if allocate_halves and stitched:
+            dev_index = d.index if d.index is not None else torch.cuda.current_device()
+            local_bytes = cfg.n_local * self.eb
+            own_bytes = (self.n_slots - cfg.n_local) * self.eb
+            self._local_phys = B.moe_vmm_create(local_bytes, dev_index)
+            self._vmm_phys.append(self._local_phys)
+            for h in range(n_halves):
+                own = B.moe_vmm_create(own_bytes, dev_index)
+                self._vmm_phys.append(own)
+                va = B.moe_vmm_map([self._local_phys, own], [local_bytes, own_bytes], dev_index)
+                self._vmm_ranges.append((va, [local_bytes, own_bytes]))
+                self.halves.append((va, self.slot_maps[h]))
+                self.wbufs.append(B.wbuf(va, self.eb, self.n_slots, E, self.slot_maps[h]))
+                self.stitched_local_pools.append(B.pool(va, self.eb, 0, cfg.n_local))
+        elif allocate_halves:
+            for h in range(n_halves):
+                base = torch.empty((self.n_slots, self.eb), dtype=torch.uint8, device=d)
+                self.halves.append((base, self.slot_maps[h]))
+                self.wbufs.append(B.wbuf(base, self.eb, self.n_slots, E, self.slot_maps[h]))
         self.compute_stream = compute_stream or torch.cuda.Stream(device=d)
         self.copy_stream = copy_stream or torch.cuda.Stream(device=d)
         self.ready = [B.moe_event_create(False) for _ in range(n_halves)]
@@ -100,6 +122,11 @@ class MoELayer:
         self.local_pool = B.pool(local, self.eb, 0, cfg.n_local)
         self.remote_pool = B.pool(remote, self.eb, cfg.n_local, cfg.E - cfg.n_local)
         torch.cuda.current_stream(self.dev).synchronize()
+        if self.stitched_local_pools:
+            # place the local experts once in the block every half maps at its head
+            B.moe_prefetch_layer(self.local_pool, list(range(cfg.n_local)), self.wbufs[0],
+                                 self.copy_stream, copy_mode=B.MOE_COPY_ANY)
+            self.copy_stream.synchronize()
 
     def set_inputs(self, x, logits) -> None:
         """x: numpy [T,H] (float32, or uint16 bf16 bits) or torch; logits numpy f32 [T,E] or torch."""
@@ -139,9 +166,15 @@ class MoELayer:
         return list(range(cfg.n_local)) + [int(e) for e in remote]
 
     def fill_half(self, half: int, ids: Sequence[int], wait_free: bool = True) -> None:
-        """Copy stream: merge the local experts (and the slot map) and prefetch the remote ones."""
+        """Copy stream: merge the local experts (and the slot map) and prefetch the remote ones.
+        With stitched halves the local experts already sit at their slots: only the map is written."""
         ws = self.free[half] if wait_free else None
-        B.moe_merge_weights(self.local_pool, ids, self.wbufs[half], self.copy_stream,
+        local = self.local_pool
+        if self.stitched_local_pools:
+            assert list(ids[: self.cfg.n_local]) == list(range(self.cfg.n_local)), \
+                "a stitched half needs every local expert at the head of the expert set"
+            local = self.stitched_local_pools[half]
+        B.moe_merge_weights(local, ids, self.wbufs[half], self.copy_stream,
                             wait_free=ws, ready=None, copy_mode=self.copy_mode)
         B.moe_prefetch_layer(self.remote_pool, ids, self.wbufs[half], self.copy_stream,
                              wait_free=None, ready=self.ready[half], copy_mode=self.copy_mode)
@@ -189,9 +222,15 @@ class MoELayer:
                     status=int(self.status.item()))
 
     def close(self) -> None:
+        self.synchronize()
         for ev in self.ready + self.free:
             B.moe_event_destroy(ev)
         self.ready, self.free = [], []
+        for va, sizes in self._vmm_ranges:
+            B.moe_vmm_unmap(va, sizes)
+        for ph in self._vmm_phys:
+            B.moe_vmm_release(ph)
+        self._vmm_ranges, self._vmm_phys = [], []
 
 
 def block_to_numpy(block: torch.Tensor) -> np.ndarray:

@@ -33,11 +33,17 @@ from .layer import MoELayer
 
 
 class MoEPipeline:
-    def __init__(self, cfg: synth.MoEConfig, device="cuda", copy_mode: int = B.MOE_COPY_SDMA):
+    """stitched=True: layer l's merged range is one virtual range over [layer l's local-expert
+    block | half (l % 2)'s own block] (moe_vmm_*), so the merge copies nothing and the copy
+    stream moves only the remote share; the halves' own blocks alternate between layers."""
+
+    def __init__(self, cfg: synth.MoEConfig, device="cuda", copy_mode: int = B.MOE_COPY_SDMA,
+                 stitched: bool = False):
         assert cfg.dtype == "bf16", "the pipeline runs the bf16 workloads"
         self.cfg = cfg
         self.dev = torch.device(device)
-        self.L = MoELayer(cfg, device=self.dev, copy_mode=copy_mode)
+        self.stitched = stitched
+        self.L = MoELayer(cfg, device=self.dev, copy_mode=copy_mode, allocate_halves=not stitched)
         L = self.L
         self.n = cfg.layers
         self.locals: List[torch.Tensor] = []
@@ -60,6 +66,29 @@ class MoEPipeline:
         self.a = torch.empty_like(self.x0)
         self.all_ids = list(range(cfg.E))
         torch.cuda.current_stream(self.dev).synchronize()
+        # merged range and local pool of each layer
+        self._ranges, self._phys = [], []
+        if stitched:
+            dev_index = self.dev.index if self.dev.index is not None else torch.cuda.current_device()
+            lb, ob = cfg.n_local * L.eb, (cfg.E - cfg.n_local) * L.eb
+            own = [B.moe_vmm_create(ob, dev_index) for _ in range(2)]
+            self._phys += own
+            self.wbufs, self.merge_pools = [], []
+            for l in range(self.n):
+                loc = B.moe_vmm_create(lb, dev_index)
+                self._phys.append(loc)
+                va = B.moe_vmm_map([loc, own[l % 2]], [lb, ob], dev_index)
+                self._ranges.append((va, [lb, ob]))
+                wb = B.wbuf(va, L.eb, cfg.E, cfg.E, L.slot_maps[l % 2])
+                self.wbufs.append(wb)
+                self.merge_pools.append(B.pool(va, L.eb, 0, cfg.n_local))
+                # the local experts of layer l are placed once in its local block
+                B.moe_prefetch_layer(self.local_pools[l], list(range(cfg.n_local)), wb,
+                                     L.copy_stream, copy_mode=B.MOE_COPY_ANY)
+            L.copy_stream.synchronize()
+        else:
+            self.wbufs = [L.wbufs[l % 2] for l in range(self.n)]
+            self.merge_pools = self.local_pools
 
     # -------------------------------------------------------------- pieces
     def fill(self, l: int, wait_free: bool = True, ev: Optional[Dict[str, list]] = None) -> None:
@@ -70,9 +99,9 @@ class MoEPipeline:
             B.moe_stream_wait_event(L.copy_stream, L.free[h])
         if ev is not None:
             B.moe_event_record(ev["c0"][l], L.copy_stream)
-        B.moe_merge_weights(self.local_pools[l], self.all_ids, L.wbufs[h], L.copy_stream,
+        B.moe_merge_weights(self.merge_pools[l], self.all_ids, self.wbufs[l], L.copy_stream,
                             wait_free=None, ready=None, copy_mode=L.copy_mode)
-        B.moe_prefetch_layer(self.remote_pools[l], self.all_ids, L.wbufs[h], L.copy_stream,
+        B.moe_prefetch_layer(self.remote_pools[l], self.all_ids, self.wbufs[l], L.copy_stream,
                              wait_free=None, ready=L.ready[h], copy_mode=L.copy_mode)
         if ev is not None:
             B.moe_event_record(ev["c1"][l], L.copy_stream)
@@ -91,7 +120,7 @@ class MoEPipeline:
         B.moe_stream_wait_event(cs, L.ready[h])
         if ev is not None:
             B.moe_event_record(ev["wait1"][l], cs)
-        B.moe_grouped_swiglu(L.x_perm, L.offsets, L.R, cfg.E, cfg.H, cfg.I, L.dt, L.wbufs[h],
+        B.moe_grouped_swiglu(L.x_perm, L.offsets, L.R, cfg.E, cfg.H, cfg.I, L.dt, self.wbufs[l],
                              L.ws_gemm, L.ws_gemm_bytes, L.y_perm, L.status, cs)
         if ev is not None and "g1" in ev:
             B.moe_event_record(ev["g1"][l], cs)
@@ -147,3 +176,12 @@ class MoEPipeline:
 
     def synchronize(self) -> None:
         self.L.synchronize()
+
+    def close(self) -> None:
+        """Release the stitched ranges and blocks (and the layer's events)."""
+        self.L.close()
+        for va, sizes in self._ranges:
+            B.moe_vmm_unmap(va, sizes)
+        for ph in self._phys:
+            B.moe_vmm_release(ph)
+        self._ranges, self._phys = [], []

@@ -19,8 +19,9 @@
  * --------------------------------
  * - Pointers named *_host are host memory; every other pointer is device
  *   memory (or pinned host memory where stated).  The caller owns all memory,
- *   streams and events; the library allocates nothing and keeps no state
- *   except the thread-local text returned by moe_last_error().
+ *   streams and events; the library allocates nothing (the moe_vmm_* set-up
+ *   calls excepted, whose purpose is to allocate) and keeps no state except
+ *   the thread-local text returned by moe_last_error().
  * - Every call only enqueues work on the stream it is given and returns; none
  *   synchronises the device.  A return value < 0 means nothing was enqueued
  *   (MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE) or a HIP call failed
@@ -173,7 +174,11 @@ int moe_permute(const int32_t* topk_idx, int T, int E, int k, const void* x, int
  *             this half is done)
  *   ready     if not NULL, recorded on the stream after the copies
  *   copy_mode MOE_COPY_SDMA or MOE_COPY_ANY
- * Copies of consecutive ids in consecutive slots are coalesced.
+ * Copies of consecutive ids in consecutive slots are coalesced, and a run
+ * whose source bytes are its destination bytes is skipped: when the merged
+ * range is stitched with the local-expert block at its head (moe_vmm_map
+ * below) and that range is passed as the local pool, the merge copies nothing
+ * and only writes the slot map.
  * Errors: MOE_ERR_ARG for unsorted or out-of-range ids, n_ids > n_slots,
  * mismatched expert_bytes or null pointers.
  */
@@ -245,6 +250,33 @@ int moe_combine(const float* y_perm, const int32_t* row_of, const float* topk_w,
 int moe_dense_gemm(const void* x, const void* w, int M, int N, int K, void* out,
                    moe_stream_t stream);
 int moe_residual_add(const void* x, const float* y, int64_t n, void* out, moe_stream_t stream);
+
+/*
+ * Split-weight management by page stitching (set-up calls: these allocate and
+ * map; never call them on the hot path).  The merged-buffer half of the
+ * contiguous-buffer panel is built as one virtual range over physical blocks
+ * placed back to back -- the local-expert block of the layer it serves, then
+ * the half's own block for fetched experts -- so the local experts need no
+ * copy (the "buffer-merge overhead" of the iteration-latency panel).
+ *   moe_vmm_granularity: the allocation granularity on `device` (block sizes
+ *                        must be multiples of it; an R1 expert block is 42 x 2 MiB)
+ *   moe_vmm_create:      a physical block of `bytes` on `device` (no mapping)
+ *   moe_vmm_map:         reserve one virtual range, map the n blocks back to
+ *                        back, grant `device` read/write; *va is its base
+ *   moe_vmm_unmap:       undo moe_vmm_map (same blocks sizes, in order)
+ *   moe_vmm_release:     free a physical block once no range maps it
+ * With such a range the expert set given to merge and prefetch must begin
+ * with every expert of the stitched local block (their slots then coincide
+ * with the block); a set that skips one would shift later experts into the
+ * block and overwrite it.
+ * Errors: MOE_ERR_ARG for empty or non-granular sizes, MOE_ERR_HIP from the runtime.
+ */
+typedef void* moe_phys_t; /* a hipMemGenericAllocationHandle_t */
+int moe_vmm_granularity(int device, size_t* bytes);
+int moe_vmm_create(int device, size_t bytes, moe_phys_t* phys);
+int moe_vmm_map(int device, const moe_phys_t* phys, const size_t* bytes, int n, void** va);
+int moe_vmm_unmap(void* va, const size_t* bytes, int n);
+int moe_vmm_release(moe_phys_t phys);
 
 /* Events and stream waits, so a caller without HIP headers can order the
  * copy stream against the compute stream.  timing != 0 makes a timing event. */

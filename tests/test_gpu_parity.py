@@ -146,17 +146,41 @@ def _sample(T, n, seed):
     return sorted(np.random.default_rng(seed).choice(T, size=n, replace=False).tolist())
 
 
-def test_r1_decode_t64():
+@pytest.mark.parametrize("stitched", [False, True], ids=["copy-merge", "stitched-merge"])
+def test_r1_decode_t64(stitched):
     cfg = synth.config("r1_decode_t64")
-    log(f"case {cfg.name}")
-    L = _run(build_layer(cfg))
-    check_sampled(cfg, L, _sample(cfg.T, 8, 1))
-    # a second step on the other half of the double buffer gives the same bits
-    y0 = L.y.clone()
-    torch.cuda.synchronize()
-    L.forward(half=1)
-    L.synchronize()
-    assert torch.equal(L.y, y0)
+    log(f"case {cfg.name} stitched={stitched}")
+    L = build_layer(cfg, stitched=stitched)
+    try:
+        _run(L)
+        check_sampled(cfg, L, _sample(cfg.T, 8, 1))
+        # a second step on the other half of the double buffer gives the same bits
+        y0 = L.y.clone()
+        torch.cuda.synchronize()
+        L.forward(half=1)
+        L.synchronize()
+        assert torch.equal(L.y, y0)
+    finally:
+        L.close()
+
+
+def test_stitched_halves_small():
+    """Both halves map the same local-expert block: merging copies nothing, results match."""
+    from grouped_gemm_weights_amd import binding as B
+    # a 1024 x 1024 expert block is 6 MiB, so the local and remote blocks are whole 2 MiB pages
+    cfg = synth.MoEConfig("bf16_stitched", T=64, H=1024, I=1024, E=16, k=4, dtype="bf16",
+                          n_local=4, seed=21)
+    g = B.moe_vmm_granularity(0)
+    if (cfg.n_local * synth.expert_block_bytes(cfg)) % g:
+        pytest.skip(f"allocation granularity {g} does not divide the local block")
+    L = build_layer(cfg, stitched=True, host_weights=True)
+    try:
+        _run(L)
+        check_full(cfg, L)
+        L.forward(half=1)
+        check_full(cfg, L)
+    finally:
+        L.close()
 
 
 def test_r1_prefill_t8192_zipf():

@@ -30,12 +30,23 @@ def _bits(t):
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def test_r1_pipeline_6x4096():
+@pytest.mark.parametrize("stitched", [True, False], ids=["stitched-merge", "copy-merge"])
+def test_r1_pipeline_6x4096(stitched):
     from grouped_gemm_weights_amd.layer import block_to_numpy
     from grouped_gemm_weights_amd.pipeline import MoEPipeline
     cfg = synth.config("r1_pipeline_6x4096")
-    log(f"case {cfg.name}")
-    P = MoEPipeline(cfg)
+    log(f"case {cfg.name} stitched={stitched}")
+    P = MoEPipeline(cfg, stitched=stitched)
+    try:
+        _check_pipeline(cfg, P, block_to_numpy)
+    finally:
+        P.close()
+        del P
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
+def _check_pipeline(cfg, P, block_to_numpy):
     tokens = sorted(np.random.default_rng(6).choice(cfg.T, size=4, replace=False).tolist())
     cap = []
 
@@ -86,6 +97,3 @@ def test_r1_pipeline_6x4096():
     log(f"end-to-end after {cfg.layers} layers: err/rms beyond {cfg.layers} bf16 spacings {e_end:.2e}, "
         f"normwise {norm_end:.2e}")
     assert e_end <= TOL["bf16"] and norm_end <= TOL["bf16"]
-    del P
-    gc.collect()
-    torch.cuda.empty_cache()
