@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--remote", choices=["routed", "all"], default="routed",
                    help="prefetch only the routed remote experts, or the whole remote share")
     p.add_argument("--copy-mode", choices=["sdma", "any"], default="sdma")
+    p.add_argument("--chunks", type=int, default=0,
+                   help="split the remote fetch into this many chunks, each with its own ready "
+                        "event, and run the grouped GEMM per chunk as it lands (0: one fetch, one GEMM)")
     p.add_argument("--merge", choices=["copy", "stitched"], default="stitched",
                    help="copy the local experts into each merged half, or stitch the local "
                         "block into the half's virtual range so the merge copies nothing")
@@ -225,6 +228,9 @@ def main():
     nev = args.steps
     mk = lambda: [B.moe_event_create(True) for _ in range(nev)]
     ev = {k: mk() for k in ("start", "rp_end", "gemm0", "gemm1", "end", "copy0", "copy1")}
+    nch = max(0, args.chunks)
+    gev = [{"g0": [B.moe_event_create(True) for _ in range(nch + 1)],
+            "g1": [B.moe_event_create(True) for _ in range(nch + 1)]} for _ in range(nev)]
 
     def step(i, timed):
         h = i % 2
@@ -236,6 +242,12 @@ def main():
         ids = L.routed_ids() if args.remote == "routed" else list(range(cfg.E))
         if timed:
             B.moe_event_record(ev["copy0"][i], ps)
+        if nch > 0:
+            L.forward_chunked(h, ids, nch, gev[i] if timed else None)
+            if timed:
+                B.moe_event_record(ev["copy1"][i], ps)
+                B.moe_event_record(ev["end"][i], cs)
+            return ids
         L.fill_half(h, ids)
         if timed:
             B.moe_event_record(ev["copy1"][i], ps)
@@ -263,8 +275,15 @@ def main():
     assert L.read_status() == 0, "device status set during the benchmark"
 
     el = lambda a, b: float(np.mean([B.moe_event_elapsed_ms(ev[a][i], ev[b][i]) for i in range(nev)]))
-    gemm_ms = el("gemm0", "gemm1")
-    combine_ms = el("gemm1", "end")
+    if nch > 0:
+        n_calls = nch + 1
+        gemm_ms = float(np.mean([sum(B.moe_event_elapsed_ms(g["g0"][c], g["g1"][c]) for c in range(n_calls))
+                                 for g in gev]))
+        combine_ms = float(np.mean([B.moe_event_elapsed_ms(g["g1"][n_calls - 1], ev["end"][i])
+                                    for i, g in enumerate(gev)]))
+    else:
+        gemm_ms = el("gemm0", "gemm1")
+        combine_ms = el("gemm1", "end")
     rp_ms = el("start", "rp_end")
     copy_ms = el("copy0", "copy1")
     layer_ms = el("start", "end")
@@ -310,7 +329,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.k, "local_experts": cfg.n_local,
                    "remote_fetch": args.remote, "copy_engine": args.copy_mode,
-                   "merge": args.merge, "parallelism": "none (1 GPU)"},
+                   "merge": args.merge, "fetch_chunks": nch, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "breakdown_ms": {"route_permute": round(rp_ms, 4), "merge_prefetch_copy": round(copy_ms, 4),
                          "grouped_swiglu": round(gemm_ms, 4), "combine": round(combine_ms, 4),

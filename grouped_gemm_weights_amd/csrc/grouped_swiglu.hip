@@ -57,6 +57,7 @@ SwigluWs swiglu_ws(int64_t R, int E, int I, moe_dtype dt) {
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(MOE_MAX_E) void plan_kernel(const int32_t* __restrict__ offsets, int E,
+                                                         int e_begin, int e_end,
                                                          int BM, const int32_t* __restrict__ slot_of,
                                                          Tile* __restrict__ tiles,
                                                          int32_t* __restrict__ n_tiles,
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(MOE_MAX_E) void plan_kernel(const int32_t* __restri
   __shared__ int32_t s[MOE_MAX_E];
   const int e = threadIdx.x;
   int nt = 0, lo = 0, cnt = 0, slot = -1;
-  if (e < E) {
+  if (e < E && e >= e_begin && e < e_end) {
     lo = offsets[e];
     cnt = offsets[e + 1] - lo;
     if (cnt > 0) {
@@ -536,6 +537,7 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int 
 
 __global__ __launch_bounds__(256) void gemm1_f32_kernel(const float* __restrict__ x_perm,
                                                         const int32_t* __restrict__ offsets, int E,
+                                                        int e_begin, int e_end,
                                                         const int32_t* __restrict__ slot_of,
                                                         const char* __restrict__ wbase,
                                                         int64_t eb, int H, int I,
@@ -545,6 +547,7 @@ __global__ __launch_bounds__(256) void gemm1_f32_kernel(const float* __restrict_
   if (idx >= static_cast<int64_t>(R) * I) return;
   const int r = static_cast<int>(idx / I), n = static_cast<int>(idx % I);
   const int e = expert_of_row(offsets, E, r);
+  if (e < e_begin || e >= e_end) return;
   const int slot = slot_of[e];
   if (slot < 0) {
     status_or(status, MOE_STATUS_EXPERT_ABSENT);
@@ -564,6 +567,7 @@ __global__ __launch_bounds__(256) void gemm1_f32_kernel(const float* __restrict_
 
 __global__ __launch_bounds__(256) void gemm2_f32_kernel(const float* __restrict__ h,
                                                         const int32_t* __restrict__ offsets, int E,
+                                                        int e_begin, int e_end,
                                                         const int32_t* __restrict__ slot_of,
                                                         const char* __restrict__ wbase,
                                                         int64_t eb, int H, int I,
@@ -573,6 +577,7 @@ __global__ __launch_bounds__(256) void gemm2_f32_kernel(const float* __restrict_
   if (idx >= static_cast<int64_t>(R) * H) return;
   const int r = static_cast<int>(idx / H), o = static_cast<int>(idx % H);
   const int e = expert_of_row(offsets, E, r);
+  if (e < e_begin || e >= e_end) return;
   const int slot = slot_of[e];
   if (slot < 0) return;
   const float* wd = reinterpret_cast<const float*>(wbase + static_cast<int64_t>(slot) * eb) +
@@ -595,11 +600,14 @@ extern "C" int moe_grouped_swiglu_workspace_size(int R, int E, int H, int I, moe
   return MOE_OK;
 }
 
-extern "C" int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int R, int E, int H,
-                                  int I, moe_dtype dtype, const moe_wbuf* w, void* ws,
-                                  size_t ws_bytes, float* y_perm, int32_t* status,
-                                  moe_stream_t stream) {
+extern "C" int moe_grouped_swiglu_range(const void* x_perm, const int32_t* offsets, int R, int E,
+                                        int H, int I, moe_dtype dtype, const moe_wbuf* w,
+                                        int e_begin, int e_end, void* ws, size_t ws_bytes,
+                                        float* y_perm, int32_t* status, moe_stream_t stream) {
   using namespace moe;
+  if (e_begin < 0 || e_end > E || e_begin > e_end)
+    return fail(MOE_ERR_ARG, "moe_grouped_swiglu: expert range [%d, %d) outside [0, %d)", e_begin,
+                e_end, E);
   if (R < 0 || E < 1 || H < 1 || I < 1 || (dtype != MOE_F32 && dtype != MOE_BF16))
     return fail(MOE_ERR_ARG, "moe_grouped_swiglu: bad sizes R=%d E=%d H=%d I=%d", R, E, H, I);
   if (E > MOE_MAX_E) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_swiglu: E=%d above %d", E, MOE_MAX_E);
@@ -626,12 +634,12 @@ extern "C" int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, in
   if (dtype == MOE_F32) {
     const int64_t n1 = static_cast<int64_t>(R) * I, n2 = static_cast<int64_t>(R) * H;
     hipLaunchKernelGGL(gemm1_f32_kernel, dim3(static_cast<unsigned>(ceil_div64(n1, 256))), dim3(256),
-                       0, s, static_cast<const float*>(x_perm), offsets, E, w->slot_of, wbase, eb,
-                       H, I, static_cast<float*>(h), status);
+                       0, s, static_cast<const float*>(x_perm), offsets, E, e_begin, e_end,
+                       w->slot_of, wbase, eb, H, I, static_cast<float*>(h), status);
     MOE_LAUNCH_CHECK("moe_grouped_swiglu: gemm1 f32");
     hipLaunchKernelGGL(gemm2_f32_kernel, dim3(static_cast<unsigned>(ceil_div64(n2, 256))), dim3(256),
-                       0, s, static_cast<const float*>(h), offsets, E, w->slot_of, wbase, eb, H, I,
-                       y_perm);
+                       0, s, static_cast<const float*>(h), offsets, E, e_begin, e_end, w->slot_of,
+                       wbase, eb, H, I, y_perm);
     MOE_LAUNCH_CHECK("moe_grouped_swiglu: gemm2 f32");
     return MOE_OK;
   }
@@ -641,8 +649,8 @@ extern "C" int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, in
   const bool decode = static_cast<int64_t>(R) <= 4 * static_cast<int64_t>(E);
   const int BM = decode ? 16 : GemmBig<true, false>::BM;
   const int64_t grid_tiles = ceil_div64(R, BM) + std::min(E, R);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(MOE_MAX_E), 0, s, offsets, E, BM, w->slot_of, tiles,
-                     n_tiles, status);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(MOE_MAX_E), 0, s, offsets, E, e_begin, e_end, BM,
+                     w->slot_of, tiles, n_tiles, status);
   MOE_LAUNCH_CHECK("moe_grouped_swiglu: plan");
 
   const int64_t HI2 = static_cast<int64_t>(H) * I * 2;  // bytes of one H x I bf16 matrix
@@ -659,6 +667,14 @@ extern "C" int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, in
     rc = Gemm2Prefill::launch(hp, I, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles, grid_tiles, 0, y_perm, H, s);
   }
   return rc;
+}
+
+extern "C" int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int R, int E, int H,
+                                  int I, moe_dtype dtype, const moe_wbuf* w, void* ws,
+                                  size_t ws_bytes, float* y_perm, int32_t* status,
+                                  moe_stream_t stream) {
+  return moe_grouped_swiglu_range(x_perm, offsets, R, E, H, I, dtype, w, 0, E, ws, ws_bytes, y_perm,
+                                  status, stream);
 }
 
 extern "C" int moe_dense_gemm(const void* x, const void* w, int M, int N, int K, void* out,

@@ -190,13 +190,61 @@ class MoELayer:
         B.moe_combine(self.y_perm, self.row_of, self.topk_w, cfg.T, cfg.k, cfg.H, self.y, cs)
         B.moe_event_record(self.free[half], cs)
 
-    def forward(self, half: int = 0, remote: str = "routed") -> None:
+    def forward(self, half: int = 0, remote: str = "routed", chunks: int = 0, ev=None) -> None:
         """One whole layer step; remote = 'routed' (fetch only the remote experts that got
-        tokens, after a count read-back) or 'all' (fetch the whole remote share)."""
+        tokens, after a count read-back) or 'all' (fetch the whole remote share).  chunks > 0
+        splits the remote fetch into that many chunks with one ready event each, and the grouped
+        GEMM runs per chunk as its weights land (the local experts first, while the copies run)."""
         self.route_permute()
         ids = self.routed_ids() if remote == "routed" else list(range(self.cfg.E))
-        self.fill_half(half, ids)
-        self.expert_compute(half)
+        if chunks <= 0:
+            self.fill_half(half, ids)
+            self.expert_compute(half)
+        else:
+            self.forward_chunked(half, ids, chunks, ev)
+
+    def _chunk_events(self, half: int, n: int):
+        if not hasattr(self, "_cev"):
+            self._cev = {}
+        lst = self._cev.setdefault(half, [])
+        while len(lst) < n:
+            lst.append(B.moe_event_create(False))
+        return lst[:n]
+
+    def forward_chunked(self, half: int, ids: Sequence[int], chunks: int, ev=None) -> None:
+        """Merge + chunked prefetch on the copy stream, per-chunk grouped GEMM on the compute
+        stream.  ``ev`` (optional): dict of timing-event lists 'g0'/'g1' (one pair per GEMM call)."""
+        cfg, cs, ps = self.cfg, self.compute_stream, self.copy_stream
+        remote_ids = [e for e in ids if e >= cfg.n_local]
+        n_ch = max(1, min(chunks, len(remote_ids))) if remote_ids else 0
+        groups = [list(g) for g in np.array_split(np.asarray(remote_ids, dtype=np.int64), n_ch)] if n_ch else []
+        bounds = [g[0] for g in groups] + [cfg.E]
+        ready = self._chunk_events(half, n_ch + 1)
+        local = self.local_pool
+        if self.stitched_local_pools:
+            assert list(ids[: cfg.n_local]) == list(range(cfg.n_local))
+            local = self.stitched_local_pools[half]
+        wb = self.wbufs[half]
+        B.moe_merge_weights(local, ids, wb, ps, wait_free=self.free[half], ready=ready[0],
+                            copy_mode=self.copy_mode)
+        rbase = self._remote_t.data_ptr()
+        for c in range(n_ch):
+            lo, hi = int(bounds[c]), int(bounds[c + 1])
+            sub = B.pool(rbase + (lo - cfg.n_local) * self.eb, self.eb, lo, hi - lo)
+            B.moe_prefetch_layer(sub, ids, wb, ps, ready=ready[c + 1], copy_mode=self.copy_mode)
+        ranges = [(0, int(bounds[0]))] + [(int(bounds[c]), int(bounds[c + 1])) for c in range(n_ch)]
+        for c, (lo, hi) in enumerate(ranges):
+            B.moe_stream_wait_event(cs, ready[c])
+            if ev is not None:
+                B.moe_event_record(ev["g0"][c], cs)
+            B.moe_grouped_swiglu_range(self.x_perm, self.offsets, self.R, cfg.E, cfg.H, cfg.I,
+                                       self.dt, wb, lo, hi, self.ws_gemm, self.ws_gemm_bytes,
+                                       self.y_perm, self.status, cs)
+            if ev is not None:
+                B.moe_event_record(ev["g1"][c], cs)
+        B.moe_combine(self.y_perm, self.row_of, self.topk_w, cfg.T, cfg.k, cfg.H, self.y, cs)
+        B.moe_event_record(self.free[half], cs)
+        self.last_ids = list(ids)
 
     def synchronize(self) -> None:
         self.compute_stream.synchronize()
@@ -223,9 +271,9 @@ class MoELayer:
 
     def close(self) -> None:
         self.synchronize()
-        for ev in self.ready + self.free:
+        for ev in self.ready + self.free + [e for l in getattr(self, "_cev", {}).values() for e in l]:
             B.moe_event_destroy(ev)
-        self.ready, self.free = [], []
+        self.ready, self.free, self._cev = [], [], {}
         for va, sizes in self._vmm_ranges:
             B.moe_vmm_unmap(va, sizes)
         for ph in self._vmm_phys:

@@ -227,6 +227,20 @@ int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int R, int E,
                        float* y_perm, int32_t* status, moe_stream_t stream);
 
 /*
+ * moe_grouped_swiglu_range -- moe_grouped_swiglu restricted to the experts
+ * [e_begin, e_end): only their rows of h and y_perm are written, the rows of
+ * other experts are left untouched, and only their slots are read.  Lets the
+ * compute stream start on the experts whose weights have arrived while the
+ * copy stream is still pulling the rest (per-chunk readiness: one ready event
+ * per chunk of the prefetch, each chunk's GEMM waiting only for its own
+ * chunk).  Calls on one stream may share the workspace.
+ * Errors: as moe_grouped_swiglu, plus MOE_ERR_ARG for a range outside [0, E].
+ */
+int moe_grouped_swiglu_range(const void* x_perm, const int32_t* offsets, int R, int E, int H, int I,
+                             moe_dtype dtype, const moe_wbuf* w, int e_begin, int e_end, void* ws,
+                             size_t ws_bytes, float* y_perm, int32_t* status, moe_stream_t stream);
+
+/*
  * moe_combine -- the weighted un-permute:
  *   y[t] = sum_{j=0..k-1} topk_w[t][j] * y_perm[row_of[t*k + j]], summed in j order, f32.
  *   y_perm device f32[T*k][H]; row_of device i32[T*k]; topk_w device f32[T][k];

@@ -164,6 +164,32 @@ def test_r1_decode_t64(stitched):
         L.close()
 
 
+@pytest.mark.parametrize("stitched", [False, True], ids=["copy-merge", "stitched-merge"])
+def test_r1_decode_t64_chunked_prefetch(stitched):
+    """Remote fetch in 4 chunks with one ready event each; the GEMM runs per chunk."""
+    cfg = synth.config("r1_decode_t64")
+    L = build_layer(cfg, stitched=stitched)
+    try:
+        L.forward(half=0, chunks=4)
+        check_sampled(cfg, L, _sample(cfg.T, 4, 11))
+        y0 = L.y.clone()
+        torch.cuda.synchronize()
+        L.forward(half=1, chunks=0)
+        L.synchronize()
+        assert torch.equal(L.y, y0)
+    finally:
+        L.close()
+
+
+@pytest.mark.parametrize("chunks", [1, 3, 7])
+def test_small_bf16_chunked_prefetch(chunks):
+    cfg = synth.MoEConfig("bf16_chunks", T=50, H=136, I=72, E=37, k=3, dtype="bf16", n_local=9,
+                          seed=1087)
+    L = build_layer(cfg)
+    L.forward(half=0, chunks=chunks)
+    check_full(cfg, L)
+
+
 def test_stitched_halves_small():
     """Both halves map the same local-expert block: merging copies nothing, results match."""
     from grouped_gemm_weights_amd import binding as B
