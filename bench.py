@@ -41,7 +41,11 @@ def parse():
     p.add_argument("--config", default="r1_decode_t64")
     p.add_argument("--remote", choices=["routed", "all"], default="routed",
                    help="prefetch only the routed remote experts, or the whole remote share")
-    p.add_argument("--copy-mode", choices=["sdma", "any"], default="sdma")
+    p.add_argument("--copy-mode", choices=["sdma", "any"], default="any",
+                   help="any: hipMemcpyDefault (the runtime's copy path); sdma: the no-compute-unit "
+                        "copy kind")
+    p.add_argument("--alt-steps", type=int, default=5,
+                   help="also time this many steps with the other copy mode (0: skip)")
     p.add_argument("--chunks", type=int, default=0,
                    help="split the remote fetch into this many chunks, each with its own ready "
                         "event, and run the grouped GEMM per chunk as it lands (0: one fetch, one GEMM)")
@@ -273,6 +277,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert L.read_status() == 0, "device status set during the benchmark"
+    alt = None
+    if args.alt_steps > 0:
+        # the same step with the other copy path, for comparison (not the reported value)
+        L.copy_mode = B.MOE_COPY_ANY if copy_mode == B.MOE_COPY_SDMA else B.MOE_COPY_SDMA
+        for i in range(2):
+            step(i, False)
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for i in range(args.alt_steps):
+            step(i, False)
+        torch.cuda.synchronize()
+        alt_s = (time.perf_counter() - ta) / args.alt_steps
+        alt = {"copy_engine": "sdma" if copy_mode == B.MOE_COPY_ANY else "any",
+               "ms_per_step": round(alt_s * 1e3, 3), "tokens_per_s": round(cfg.T / alt_s, 1)}
+        L.copy_mode = copy_mode
 
     el = lambda a, b: float(np.mean([B.moe_event_elapsed_ms(ev[a][i], ev[b][i]) for i in range(nev)]))
     if nch > 0:
@@ -338,6 +357,8 @@ def main():
         "active_experts": n_active,
         "gemm_TFLOPs": round(gemm_tflops, 2),
     }
+    if alt is not None:
+        result["other_copy_engine"] = alt
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_sample_tokens)
     L.close()
