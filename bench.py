@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--chunks", type=int, default=0,
                    help="split the remote fetch into this many chunks, each with its own ready "
                         "event, and run the grouped GEMM per chunk as it lands (0: one fetch, one GEMM)")
+    p.add_argument("--gather", choices=["separate", "fused"], default="fused",
+                   help="separate: moe_permute writes x_perm; fused: the grouped GEMM gathers its rows "
+                        "from x on load (moe_grouped_swiglu_gathered)")
     p.add_argument("--merge", choices=["copy", "stitched"], default="stitched",
                    help="copy the local experts into each merged half, or stitch the local "
                         "block into the half's virtual range so the merge copies nothing")
@@ -101,7 +104,8 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     from grouped_gemm_weights_amd import synth
     from grouped_gemm_weights_amd.pipeline import MoEPipeline
 
-    P = MoEPipeline(cfg, device=dev, copy_mode=copy_mode, stitched=args.merge == "stitched")
+    P = MoEPipeline(cfg, device=dev, copy_mode=copy_mode, stitched=args.merge == "stitched",
+                    fused_gather=args.gather == "fused")
     n = cfg.layers
     keys = ("c0", "c1", "wait0", "wait1", "d0", "m1", "g1")
     mk = lambda: {k: [B.moe_event_create(True) for _ in range(n)] for k in keys}
@@ -148,7 +152,7 @@ def bench_pipeline(args, cfg, dev, copy_mode):
         "config": {"workload": cfg.name, "layers": n, "tokens": cfg.T, "hidden": cfg.H,
                    "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k,
                    "local_experts": cfg.n_local, "copy_engine": args.copy_mode,
-                   "merge": args.merge, "parallelism": "none (1 GPU)"},
+                   "merge": args.merge, "gather": args.gather, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "moe_grouped_swiglu, pipelined layers (with the copy running)",
@@ -222,7 +226,8 @@ def main():
     if cfg.layers != 1:
         print(json.dumps(bench_pipeline(args, cfg, dev, copy_mode)), flush=True)
         return
-    L = MoELayer(cfg, device=dev, copy_mode=copy_mode, stitched=args.merge == "stitched")
+    L = MoELayer(cfg, device=dev, copy_mode=copy_mode, stitched=args.merge == "stitched",
+                 fused_gather=args.gather == "fused")
     local = synth.pool_torch(cfg, 0, 0, cfg.n_local, dev)
     remote = synth.pool_torch(cfg, 0, cfg.n_local, cfg.E - cfg.n_local, dev)
     L.set_pools(local, remote)
@@ -258,8 +263,7 @@ def main():
         B.moe_stream_wait_event(cs, L.ready[h])
         if timed:
             B.moe_event_record(ev["gemm0"][i], cs)
-        B.moe_grouped_swiglu(L.x_perm, L.offsets, L.R, cfg.E, cfg.H, cfg.I, L.dt, L.wbufs[h],
-                             L.ws_gemm, L.ws_gemm_bytes, L.y_perm, L.status, cs)
+        L.grouped(L.wbufs[h])
         if timed:
             B.moe_event_record(ev["gemm1"][i], cs)
         B.moe_combine(L.y_perm, L.row_of, L.topk_w, cfg.T, cfg.k, cfg.H, L.y, cs)
@@ -348,7 +352,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.k, "local_experts": cfg.n_local,
                    "remote_fetch": args.remote, "copy_engine": args.copy_mode,
-                   "merge": args.merge, "fetch_chunks": nch, "parallelism": "none (1 GPU)"},
+                   "merge": args.merge, "gather": args.gather, "fetch_chunks": nch, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "breakdown_ms": {"route_permute": round(rp_ms, 4), "merge_prefetch_copy": round(copy_ms, 4),
                          "grouped_swiglu": round(gemm_ms, 4), "combine": round(combine_ms, 4),

@@ -24,7 +24,7 @@ MOE_COPY_SDMA, MOE_COPY_ANY = 0, 1
 EXPORTS = (
     "moe_route", "moe_permute_workspace_size", "moe_permute", "moe_merge_weights",
     "moe_prefetch_layer", "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu",
-    "moe_grouped_swiglu_range",
+    "moe_grouped_swiglu_range", "moe_grouped_swiglu_gathered",
     "moe_combine", "moe_dense_gemm", "moe_residual_add", "moe_event_create",
     "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms", "moe_stream_wait_event",
     "moe_last_error", "moe_version", "moe_vmm_granularity", "moe_vmm_create", "moe_vmm_map",
@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
         "moe_grouped_swiglu_workspace_size": [I, I, I, I, I, PSZ],
         "moe_grouped_swiglu": [P, P, I, I, I, I, I, ctypes.POINTER(MoeWbuf), P, SZ, P, P, P],
         "moe_grouped_swiglu_range": [P, P, I, I, I, I, I, ctypes.POINTER(MoeWbuf), I, I, P, SZ, P, P, P],
+        "moe_grouped_swiglu_gathered": [P, P, I, P, I, I, I, I, I, ctypes.POINTER(MoeWbuf), I, I, P, SZ,
+                                        P, P, P],
         "moe_combine": [P, P, P, I, I, I, P, P],
         "moe_dense_gemm": [P, P, I, I, I, P, P],
         "moe_residual_add": [P, P, I64, P, P],
@@ -188,6 +190,14 @@ def moe_grouped_swiglu_range(x_perm, offsets, R, E, H, I, dtype, w: MoeWbuf, e_b
            lib.moe_grouped_swiglu_range(ptr(x_perm), ptr(offsets), R, E, H, I, dtype, ctypes.byref(w),
                                         e_begin, e_end, ptr(ws), ws_bytes, ptr(y_perm), ptr(status),
                                         stream_handle(stream)))
+
+
+def moe_grouped_swiglu_gathered(x, src_of, k, offsets, R, E, H, I, dtype, w: MoeWbuf, e_begin, e_end,
+                                ws, ws_bytes, y_perm, status=None, stream=None):
+    _check("moe_grouped_swiglu_gathered",
+           lib.moe_grouped_swiglu_gathered(ptr(x), ptr(src_of), k, ptr(offsets), R, E, H, I, dtype,
+                                           ctypes.byref(w), e_begin, e_end, ptr(ws), ws_bytes,
+                                           ptr(y_perm), ptr(status), stream_handle(stream)))
 
 
 def moe_combine(y_perm, row_of, topk_w, T, k, H, y, stream=None):

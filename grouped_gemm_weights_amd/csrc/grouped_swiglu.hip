@@ -107,7 +107,8 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)
 //   !DUAL  out = A B0^T, as f32 (OUT_BF16 = false) or bf16
 template <int BM, int BN, int BK, int WM, int WN, bool DUAL, bool OUT_BF16>
 __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, int lda, const char* __restrict__ wbase, int64_t expert_bytes,
+    const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ a_index, int a_div,
+    const char* __restrict__ wbase, int64_t expert_bytes,
     int64_t b0_off, int64_t b1_off, int N, int K, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, int dense_M, void* __restrict__ out, int ldo) {
   constexpr int NT = WM * WN * kWave;
@@ -141,13 +142,23 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
   const char* wexp = wbase + static_cast<int64_t>(tile.slot) * expert_bytes;
   const uint16_t* B0 = reinterpret_cast<const uint16_t*>(wexp + b0_off);
   const uint16_t* B1 = reinterpret_cast<const uint16_t*>(wexp + b1_off);
-  const uint16_t* Arow = A + static_cast<int64_t>(tile.row0) * lda;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int wm0 = (wave / WN) * (BM / WM);
   const int wn0 = (wave % WN) * (BN / WN);
+
+  // A rows this thread loads: row r of the tile is A row tile.row0 + r, or, gathered,
+  // A row a_index[tile.row0 + r] / a_div (rows past the tile read row 0, never stored)
+  const uint16_t* a_row[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int r = (tid + i * NT) / KC;
+    int src = tile.row0 + (r < tile.rows ? r : 0);
+    if (a_index) src = a_index[src] / a_div;
+    a_row[i] = A + static_cast<int64_t>(src) * lda;
+  }
 
   uint4 ra[CA], rb[CB];
 
@@ -158,7 +169,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
       const int r = c / KC, k = (k0) + (c % KC) * 8;                                          \
       ra[i] = make_uint4(0, 0, 0, 0);                                                         \
       if (r < tile.rows && k < K)                                                             \
-        ra[i] = *reinterpret_cast<const uint4*>(Arow + static_cast<int64_t>(r) * lda + k);    \
+        ra[i] = *reinterpret_cast<const uint4*>(a_row[i] + k);                               \
     }                                                                                         \
     _Pragma("unroll") for (int i = 0; i < CB; ++i) {                                          \
       const int c = tid + i * NT;                                                             \
@@ -268,7 +279,8 @@ struct GemmShape {
   static constexpr size_t kLds =
       2 * static_cast<size_t>(BM + (DUAL ? 2 : 1) * BN) * (BK + 8) * sizeof(uint16_t);
 
-  static int launch(const uint16_t* A, int lda, const char* wbase, int64_t expert_bytes,
+  static int launch(const uint16_t* A, int lda, const int32_t* a_index, int a_div,
+                    const char* wbase, int64_t expert_bytes,
                     int64_t b0_off, int64_t b1_off, int N, int K, const Tile* tiles,
                     const int32_t* n_tiles, int64_t grid_tiles, int dense_M, void* out, int ldo,
                     hipStream_t s) {
@@ -282,8 +294,8 @@ struct GemmShape {
     }
     if (grid_tiles <= 0) return MOE_OK;
     dim3 grid(static_cast<unsigned>(grid_tiles), static_cast<unsigned>(ceil_div(N, BN)));
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLds, s, A, lda, wbase, expert_bytes, b0_off,
-                       b1_off, N, K, tiles, n_tiles, dense_M, out, ldo);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLds, s, A, lda, a_index, a_div, wbase,
+                       expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles, dense_M, out, ldo);
     MOE_LAUNCH_CHECK("gemm_bf16_kernel launch");
     return MOE_OK;
   }
@@ -312,7 +324,8 @@ constexpr int kMGroup = 4;
 
 template <bool DUAL, bool OUT_BF16>
 __global__ __launch_bounds__(512) void gemm_big_kernel(
-    const uint16_t* __restrict__ A, int lda, const char* __restrict__ wbase, int64_t expert_bytes,
+    const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ a_index, int a_div,
+    const char* __restrict__ wbase, int64_t expert_bytes,
     int64_t b0_off, int64_t b1_off, int N, int K, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, int dense_M, void* __restrict__ out, int ldo) {
   constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
@@ -354,7 +367,6 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
   const char* wexp = wbase + static_cast<int64_t>(tile.slot) * expert_bytes;
   const uint16_t* B0 = reinterpret_cast<const uint16_t*>(wexp + b0_off);
   const uint16_t* B1 = reinterpret_cast<const uint16_t*>(wexp + b1_off);
-  const uint16_t* Arow = A + static_cast<int64_t>(tile.row0) * lda;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -371,7 +383,10 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
     const int c = tid + i * NT;
     const int r = c / KC, kc = c % KC;
     a_ok[i] = r < tile.rows;
-    a_src[i] = Arow + static_cast<int64_t>(a_ok[i] ? r : 0) * lda + kc * 8;
+    // tile row r is A row tile.row0 + r, or, gathered, A row a_index[tile.row0 + r] / a_div
+    int src = tile.row0 + (a_ok[i] ? r : 0);
+    if (a_index) src = a_index[src] / a_div;
+    a_src[i] = A + static_cast<int64_t>(src) * lda + kc * 8;
     a_lds[i] = r * LDS_LD + kc * 8;
   }
   const uint16_t* b_src[CB];
@@ -490,7 +505,8 @@ struct GemmBig {
   static constexpr size_t kLds = 2 * static_cast<size_t>(256 + 256) * (64 + 8) * sizeof(uint16_t);
 
   // grid_m: upper bound on the number of m-tiles
-  static int launch(const uint16_t* A, int lda, const char* wbase, int64_t expert_bytes,
+  static int launch(const uint16_t* A, int lda, const int32_t* a_index, int a_div,
+                    const char* wbase, int64_t expert_bytes,
                     int64_t b0_off, int64_t b1_off, int N, int K, const Tile* tiles,
                     const int32_t* n_tiles, int64_t grid_m, int dense_M, void* out, int ldo,
                     hipStream_t s) {
@@ -506,8 +522,9 @@ struct GemmBig {
     const int outn = DUAL ? 128 : 256;
     const int64_t items = grid_m * ceil_div(N, outn);
     const int64_t blocks = ceil_div64(items, kXcds) * kXcds;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(512), kLds, s, A, lda, wbase,
-                       expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles, dense_M, out, ldo);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(512), kLds, s, A, lda, a_index,
+                       a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles, dense_M,
+                       out, ldo);
     MOE_LAUNCH_CHECK("gemm_big_kernel launch");
     return MOE_OK;
   }
@@ -536,6 +553,7 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int 
 }
 
 __global__ __launch_bounds__(256) void gemm1_f32_kernel(const float* __restrict__ x_perm,
+                                                        const int32_t* __restrict__ a_index, int a_div,
                                                         const int32_t* __restrict__ offsets, int E,
                                                         int e_begin, int e_end,
                                                         const int32_t* __restrict__ slot_of,
@@ -556,7 +574,7 @@ __global__ __launch_bounds__(256) void gemm1_f32_kernel(const float* __restrict_
   const float* W = reinterpret_cast<const float*>(wbase + static_cast<int64_t>(slot) * eb);
   const float* wg = W + static_cast<int64_t>(n) * H;
   const float* wu = W + static_cast<int64_t>(H) * I + static_cast<int64_t>(n) * H;
-  const float* x = x_perm + static_cast<int64_t>(r) * H;
+  const float* x = x_perm + static_cast<int64_t>(a_index ? a_index[r] / a_div : r) * H;
   float g = 0.f, u = 0.f;
   for (int c = 0; c < H; ++c) {
     g = fmaf(x[c], wg[c], g);
@@ -600,11 +618,15 @@ extern "C" int moe_grouped_swiglu_workspace_size(int R, int E, int H, int I, moe
   return MOE_OK;
 }
 
-extern "C" int moe_grouped_swiglu_range(const void* x_perm, const int32_t* offsets, int R, int E,
-                                        int H, int I, moe_dtype dtype, const moe_wbuf* w,
-                                        int e_begin, int e_end, void* ws, size_t ws_bytes,
-                                        float* y_perm, int32_t* status, moe_stream_t stream) {
-  using namespace moe;
+namespace moe {
+namespace {
+
+// The grouped SwiGLU over experts [e_begin, e_end).  A row r of the gate/up GEMM is row r of
+// x_perm, or, when a_index is given, row a_index[r] / a_div of x (the gather done on load).
+int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
+                        const int32_t* offsets, int R, int E, int H, int I, moe_dtype dtype,
+                        const moe_wbuf* w, int e_begin, int e_end, void* ws, size_t ws_bytes,
+                        float* y_perm, int32_t* status, moe_stream_t stream) {
   if (e_begin < 0 || e_end > E || e_begin > e_end)
     return fail(MOE_ERR_ARG, "moe_grouped_swiglu: expert range [%d, %d) outside [0, %d)", e_begin,
                 e_end, E);
@@ -634,7 +656,8 @@ extern "C" int moe_grouped_swiglu_range(const void* x_perm, const int32_t* offse
   if (dtype == MOE_F32) {
     const int64_t n1 = static_cast<int64_t>(R) * I, n2 = static_cast<int64_t>(R) * H;
     hipLaunchKernelGGL(gemm1_f32_kernel, dim3(static_cast<unsigned>(ceil_div64(n1, 256))), dim3(256),
-                       0, s, static_cast<const float*>(x_perm), offsets, E, e_begin, e_end,
+                       0, s, static_cast<const float*>(x_perm), a_index, a_div, offsets, E,
+                       e_begin, e_end,
                        w->slot_of, wbase, eb, H, I, static_cast<float*>(h), status);
     MOE_LAUNCH_CHECK("moe_grouped_swiglu: gemm1 f32");
     hipLaunchKernelGGL(gemm2_f32_kernel, dim3(static_cast<unsigned>(ceil_div64(n2, 256))), dim3(256),
@@ -658,16 +681,44 @@ extern "C" int moe_grouped_swiglu_range(const void* x_perm, const int32_t* offse
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   int rc;
   if (decode) {
-    rc = Gemm1Decode::launch(xp, H, wbase, eb, 0, HI2, I, H, tiles, n_tiles, grid_tiles, 0, h, I, s);
+    rc = Gemm1Decode::launch(xp, H, a_index, a_div, wbase, eb, 0, HI2, I, H, tiles, n_tiles,
+                             grid_tiles, 0, h, I, s);
     if (rc) return rc;
-    rc = Gemm2Decode::launch(hp, I, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles, grid_tiles, 0, y_perm, H, s);
+    rc = Gemm2Decode::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
+                             grid_tiles, 0, y_perm, H, s);
   } else {
-    rc = Gemm1Prefill::launch(xp, H, wbase, eb, 0, HI2, I, H, tiles, n_tiles, grid_tiles, 0, h, I, s);
+    rc = Gemm1Prefill::launch(xp, H, a_index, a_div, wbase, eb, 0, HI2, I, H, tiles, n_tiles,
+                              grid_tiles, 0, h, I, s);
     if (rc) return rc;
-    rc = Gemm2Prefill::launch(hp, I, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles, grid_tiles, 0, y_perm, H, s);
+    rc = Gemm2Prefill::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
+                              grid_tiles, 0, y_perm, H, s);
   }
   return rc;
 }
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_grouped_swiglu_range(const void* x_perm, const int32_t* offsets, int R, int E,
+                                        int H, int I, moe_dtype dtype, const moe_wbuf* w,
+                                        int e_begin, int e_end, void* ws, size_t ws_bytes,
+                                        float* y_perm, int32_t* status, moe_stream_t stream) {
+  return moe::grouped_swiglu_impl(x_perm, nullptr, 1, offsets, R, E, H, I, dtype, w, e_begin, e_end,
+                                  ws, ws_bytes, y_perm, status, stream);
+}
+
+extern "C" int moe_grouped_swiglu_gathered(const void* x, const int32_t* src_of, int k,
+                                           const int32_t* offsets, int R, int E, int H, int I,
+                                           moe_dtype dtype, const moe_wbuf* w, int e_begin,
+                                           int e_end, void* ws, size_t ws_bytes, float* y_perm,
+                                           int32_t* status, moe_stream_t stream) {
+  using namespace moe;
+  if (k < 1) return fail(MOE_ERR_ARG, "moe_grouped_swiglu_gathered: k=%d", k);
+  if (R > 0 && !src_of) return fail(MOE_ERR_ARG, "moe_grouped_swiglu_gathered: null src_of");
+  return grouped_swiglu_impl(x, src_of, k, offsets, R, E, H, I, dtype, w, e_begin, e_end, ws,
+                             ws_bytes, y_perm, status, stream);
+}
+
 
 extern "C" int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int R, int E, int H,
                                   int I, moe_dtype dtype, const moe_wbuf* w, void* ws,
@@ -685,7 +736,7 @@ extern "C" int moe_dense_gemm(const void* x, const void* w, int M, int N, int K,
     return fail(MOE_ERR_UNSUPPORTED, "moe_dense_gemm: N=%d and K=%d must be multiples of 8", N, K);
   if (M == 0) return MOE_OK;
   if (!x || !w || !out) return fail(MOE_ERR_ARG, "moe_dense_gemm: null pointer");
-  return DenseBf16::launch(static_cast<const uint16_t*>(x), K, static_cast<const char*>(w), 0, 0, 0,
+  return DenseBf16::launch(static_cast<const uint16_t*>(x), K, nullptr, 1, static_cast<const char*>(w), 0, 0, 0,
                            N, K, nullptr, nullptr, ceil_div(M, DenseBf16::BM), M, out, N,
                            as_stream(stream));
 }

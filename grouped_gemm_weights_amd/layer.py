@@ -45,12 +45,14 @@ class MoELayer:
     def __init__(self, cfg: MoEConfig, device="cuda", n_slots: Optional[int] = None,
                  n_halves: int = 2, compute_stream=None, copy_stream=None,
                  copy_mode: int = B.MOE_COPY_SDMA, stitched: bool = False,
-                 allocate_halves: bool = True):
+                 allocate_halves: bool = True, fused_gather: bool = False):
         """stitched: each half is one virtual range over [the local-expert block | the half's own
         block], so merging the local experts copies nothing (page stitching, moe_vmm_*).
-        allocate_halves=False leaves the halves to the caller (the pipeline builds per-layer ranges)."""
+        allocate_halves=False leaves the halves to the caller (the pipeline builds per-layer ranges).
+        fused_gather: the grouped GEMM reads its rows from x through src_of, and x_perm is not built."""
         self.cfg = cfg
         self.stitched = stitched
+        self.fused_gather = fused_gather
         self.dev = torch.device(device)
         self.copy_mode = copy_mode
         T, E, k, H, I = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I
@@ -69,7 +71,8 @@ class MoELayer:
         self.offsets = torch.empty((E + 1,), **i32)
         self.row_of = torch.empty((R,), **i32)
         self.src_of = torch.empty((R,), **i32)
-        self.x_perm = torch.empty((R, H), dtype=tdt, device=d)
+        # with the gather fused into the GEMM's loads, x_perm is never written
+        self.x_perm = torch.empty((1 if fused_gather else R, H), dtype=tdt, device=d)
         self.y_perm = torch.empty((R, H), dtype=torch.float32, device=d)
         self.y = torch.empty((T, H), dtype=torch.float32, device=d)
         self.status = torch.zeros((1,), **i32)
@@ -151,8 +154,23 @@ class MoELayer:
         cfg, cs = self.cfg, self.compute_stream
         B.moe_route(self.logits, cfg.T, cfg.E, cfg.k, self.topk_idx, self.topk_w, self.status, cs)
         B.moe_permute(self.topk_idx, cfg.T, cfg.E, cfg.k, self.x, cfg.H, self.dt, self.counts,
-                      self.offsets, self.row_of, self.src_of, self.x_perm, self.ws_perm,
+                      self.offsets, self.row_of, self.src_of,
+                      None if self.fused_gather else self.x_perm, self.ws_perm,
                       self.ws_perm_bytes, self.status, cs)
+
+    def grouped(self, wbuf, e_begin: int = 0, e_end: Optional[int] = None, stream=None) -> None:
+        """The grouped SwiGLU GEMM over experts [e_begin, e_end) of ``wbuf`` into y_perm."""
+        cfg = self.cfg
+        e_end = cfg.E if e_end is None else e_end
+        cs = self.compute_stream if stream is None else stream
+        if self.fused_gather:
+            B.moe_grouped_swiglu_gathered(self.x, self.src_of, cfg.k, self.offsets, self.R, cfg.E,
+                                          cfg.H, cfg.I, self.dt, wbuf, e_begin, e_end, self.ws_gemm,
+                                          self.ws_gemm_bytes, self.y_perm, self.status, cs)
+        else:
+            B.moe_grouped_swiglu_range(self.x_perm, self.offsets, self.R, cfg.E, cfg.H, cfg.I,
+                                       self.dt, wbuf, e_begin, e_end, self.ws_gemm,
+                                       self.ws_gemm_bytes, self.y_perm, self.status, cs)
 
     def routed_ids(self) -> Sequence[int]:
         """Read counts back (one small copy and a sync) and return the expert set of the buffer:
@@ -180,13 +198,11 @@ class MoELayer:
                              wait_free=None, ready=self.ready[half], copy_mode=self.copy_mode)
         self.last_ids = list(ids)
 
-    def expert_compute(self, half: int, x_perm=None) -> None:
+    def expert_compute(self, half: int) -> None:
         """Compute stream: wait for the half, grouped SwiGLU GEMM, combine, release the half."""
         cfg, cs = self.cfg, self.compute_stream
         B.moe_stream_wait_event(cs, self.ready[half])
-        B.moe_grouped_swiglu(self.x_perm if x_perm is None else x_perm, self.offsets, self.R, cfg.E,
-                             cfg.H, cfg.I, self.dt, self.wbufs[half], self.ws_gemm,
-                             self.ws_gemm_bytes, self.y_perm, self.status, cs)
+        self.grouped(self.wbufs[half])
         B.moe_combine(self.y_perm, self.row_of, self.topk_w, cfg.T, cfg.k, cfg.H, self.y, cs)
         B.moe_event_record(self.free[half], cs)
 
@@ -237,9 +253,7 @@ class MoELayer:
             B.moe_stream_wait_event(cs, ready[c])
             if ev is not None:
                 B.moe_event_record(ev["g0"][c], cs)
-            B.moe_grouped_swiglu_range(self.x_perm, self.offsets, self.R, cfg.E, cfg.H, cfg.I,
-                                       self.dt, wb, lo, hi, self.ws_gemm, self.ws_gemm_bytes,
-                                       self.y_perm, self.status, cs)
+            self.grouped(wb, lo, hi)
             if ev is not None:
                 B.moe_event_record(ev["g1"][c], cs)
         B.moe_combine(self.y_perm, self.row_of, self.topk_w, cfg.T, cfg.k, cfg.H, self.y, cs)

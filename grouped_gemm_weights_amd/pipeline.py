@@ -38,12 +38,13 @@ class MoEPipeline:
     stream moves only the remote share; the halves' own blocks alternate between layers."""
 
     def __init__(self, cfg: synth.MoEConfig, device="cuda", copy_mode: int = B.MOE_COPY_SDMA,
-                 stitched: bool = False):
+                 stitched: bool = False, fused_gather: bool = False):
         assert cfg.dtype == "bf16", "the pipeline runs the bf16 workloads"
         self.cfg = cfg
         self.dev = torch.device(device)
         self.stitched = stitched
-        self.L = MoELayer(cfg, device=self.dev, copy_mode=copy_mode, allocate_halves=not stitched)
+        self.L = MoELayer(cfg, device=self.dev, copy_mode=copy_mode, allocate_halves=not stitched,
+                          fused_gather=fused_gather)
         L = self.L
         self.n = cfg.layers
         self.locals: List[torch.Tensor] = []
@@ -120,8 +121,7 @@ class MoEPipeline:
         B.moe_stream_wait_event(cs, L.ready[h])
         if ev is not None:
             B.moe_event_record(ev["wait1"][l], cs)
-        B.moe_grouped_swiglu(L.x_perm, L.offsets, L.R, cfg.E, cfg.H, cfg.I, L.dt, self.wbufs[l],
-                             L.ws_gemm, L.ws_gemm_bytes, L.y_perm, L.status, cs)
+        L.grouped(self.wbufs[l])
         if ev is not None and "g1" in ev:
             B.moe_event_record(ev["g1"][l], cs)
         B.moe_combine(L.y_perm, L.row_of, L.topk_w, cfg.T, cfg.k, cfg.H, L.y, cs)

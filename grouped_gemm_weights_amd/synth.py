@@ -85,6 +85,11 @@ CONFIGS = {
     "r1_pipeline_6x4096": MoEConfig("r1_pipeline_6x4096", T=4096, seed=505, layers=6,
                                     dense_standin=True, **_R1),
 }
+# DWDP3: a 3-rank group holds 86 of the 256 experts locally and fetches 170
+_R1_3 = dict(_R1, n_local=86)
+CONFIGS["r1_decode_t64_dwdp3"] = MoEConfig("r1_decode_t64_dwdp3", T=64, seed=202, **_R1_3)
+CONFIGS["r1_pipeline_6x4096_dwdp3"] = MoEConfig("r1_pipeline_6x4096_dwdp3", T=4096, seed=505,
+                                                 layers=6, dense_standin=True, **_R1_3)
 
 
 def config(name: str) -> MoEConfig:

@@ -241,6 +241,20 @@ int moe_grouped_swiglu_range(const void* x_perm, const int32_t* offsets, int R, 
                              size_t ws_bytes, float* y_perm, int32_t* status, moe_stream_t stream);
 
 /*
+ * moe_grouped_swiglu_gathered -- moe_grouped_swiglu_range with the row gather
+ * of moe_permute folded into the GEMM's operand loads: row r of the gate/up
+ * GEMM is read from x[src_of[r] / k] instead of x_perm[r], so moe_permute may
+ * be called with x_perm = NULL and the [T*k][H] copy is never written.
+ *   x      device [T][H] dtype; src_of device i32[T*k] (from moe_permute); k >= 1
+ *   other arguments as moe_grouped_swiglu_range.
+ * Errors: as moe_grouped_swiglu_range, plus MOE_ERR_ARG for k < 1 or a null src_of.
+ */
+int moe_grouped_swiglu_gathered(const void* x, const int32_t* src_of, int k, const int32_t* offsets,
+                                int R, int E, int H, int I, moe_dtype dtype, const moe_wbuf* w,
+                                int e_begin, int e_end, void* ws, size_t ws_bytes, float* y_perm,
+                                int32_t* status, moe_stream_t stream);
+
+/*
  * moe_combine -- the weighted un-permute:
  *   y[t] = sum_{j=0..k-1} topk_w[t][j] * y_perm[row_of[t*k + j]], summed in j order, f32.
  *   y_perm device f32[T*k][H]; row_of device i32[T*k]; topk_w device f32[T][k];

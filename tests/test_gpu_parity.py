@@ -164,6 +164,18 @@ def test_r1_decode_t64(stitched):
         L.close()
 
 
+def test_r1_decode_t64_dwdp3_split():
+    """The 3-rank split: 86 local experts, 170 fetched; stitched merge."""
+    cfg = synth.config("r1_decode_t64_dwdp3")
+    L = build_layer(cfg, stitched=True)
+    try:
+        _run(L)
+        out = check_sampled(cfg, L, _sample(cfg.T, 4, 5))
+        assert L.last_ids[: cfg.n_local] == list(range(cfg.n_local))
+    finally:
+        L.close()
+
+
 @pytest.mark.parametrize("stitched", [False, True], ids=["copy-merge", "stitched-merge"])
 def test_r1_decode_t64_chunked_prefetch(stitched):
     """Remote fetch in 4 chunks with one ready event each; the GEMM runs per chunk."""
@@ -188,6 +200,45 @@ def test_small_bf16_chunked_prefetch(chunks):
     L = build_layer(cfg)
     L.forward(half=0, chunks=chunks)
     check_full(cfg, L)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,n_local", [
+    (50, 136, 72, 37, 3, 9),       # decode tiles, ragged
+    (300, 128, 64, 8, 2, 2),       # prefill tiles
+    (64, 256, 512, 8, 2, 4),       # fp32 is covered below
+])
+def test_fused_gather_small(T, H, I, E, k, n_local):
+    cfg = synth.MoEConfig(f"bf16_gather_T{T}", T=T, H=H, I=I, E=E, k=k, dtype="bf16",
+                          n_local=n_local, seed=1000 + T + E)
+    L = build_layer(cfg, fused_gather=True)
+    L.forward(half=0)
+    out = L.outputs()
+    x = synth.activations(cfg)
+    logits = synth.logits(cfg)
+    check_routing(cfg, out, logits)
+    ref = O.moe_layer(x, logits, cfg.k, weights_fn(L), cfg.H, cfg.I, round_h=True)
+    assert rel_err(out["y"], ref["y"]) <= TOL["bf16"]
+    assert rel_err(out["y_perm"], ref["y_perm"]) <= TOL["bf16"]
+
+
+def test_fused_gather_tiny_fp32():
+    cfg = synth.config("tiny_fp32_t64")
+    L = build_layer(cfg, fused_gather=True)
+    L.forward(half=0)
+    out = L.outputs()
+    ref = O.moe_layer(synth.activations(cfg), synth.logits(cfg), cfg.k, weights_fn(L), cfg.H, cfg.I,
+                      round_h=False)
+    assert rel_err(out["y"], ref["y"]) <= TOL["f32"]
+
+
+def test_r1_prefill_t16384_fused_gather():
+    cfg = synth.config("r1_prefill_t16384")
+    L = build_layer(cfg, stitched=True, fused_gather=True)
+    try:
+        L.forward(half=0, remote="all")
+        check_sampled(cfg, L, _sample(cfg.T, 4, 13), check_xperm=False)
+    finally:
+        L.close()
 
 
 def test_stitched_halves_small():
