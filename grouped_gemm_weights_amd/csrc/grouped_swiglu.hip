@@ -100,221 +100,12 @@ __global__ __launch_bounds__(MOE_MAX_E) void plan_kernel(const int32_t* __restri
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
-// out[tile rows][n0 .. n0+BN) for one (tile, column block).
-//   A      bf16 rows, row stride lda; rows of this tile start at tile.row0
-//   B0/B1  bf16 [N][K] weight matrices at wbase + slot*expert_bytes + b?_off
-//   DUAL   gemm1: B0 = Wg, B1 = Wu, out = bf16(silu(A B0^T) * (A B1^T))
-//   !DUAL  out = A B0^T, as f32 (OUT_BF16 = false) or bf16
-template <int BM, int BN, int BK, int WM, int WN, bool DUAL, bool OUT_BF16>
-__global__ __launch_bounds__(WM* WN* kWave) void gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ a_index, int a_div,
-    const char* __restrict__ wbase, int64_t expert_bytes,
-    int64_t b0_off, int64_t b1_off, int N, int K, const Tile* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, int dense_M, void* __restrict__ out, int ldo) {
-  constexpr int NT = WM * WN * kWave;
-  constexpr int NB = DUAL ? 2 : 1;
-  constexpr int LDS_LD = BK + 8;             // row stride in elements (16-byte pad)
-  constexpr int KC = BK / 8;                 // 16-byte chunks per row per K step
-  constexpr int CA = BM * KC / NT;           // A chunks per thread per K step
-  constexpr int CB = NB * BN * KC / NT;      // B chunks per thread per K step
-  constexpr int TM = BM / WM / 16;
-  constexpr int TN = BN / WN / 16;
-  static_assert(CA * NT == BM * KC, "A tile must split evenly over the threads");
-  static_assert(CB * NT == NB * BN * KC, "B tile must split evenly over the threads");
-  static_assert(TM >= 1 && TN >= 1 && BK % 32 == 0, "bad tile shape");
-
-  Tile tile;
-  if (tiles) {
-    if (static_cast<int>(blockIdx.x) >= *n_tiles) return;
-    tile = tiles[blockIdx.x];
-  } else {
-    tile.expert = 0;
-    tile.row0 = blockIdx.x * BM;
-    tile.rows = min(BM, dense_M - tile.row0);
-    tile.slot = 0;
-  }
-  const int n0 = blockIdx.y * BN;
-
-  extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* As = smem;                         // [2][BM][LDS_LD]
-  uint16_t* Bs = smem + 2 * BM * LDS_LD;       // [2][NB*BN][LDS_LD]
-
-  const char* wexp = wbase + static_cast<int64_t>(tile.slot) * expert_bytes;
-  const uint16_t* B0 = reinterpret_cast<const uint16_t*>(wexp + b0_off);
-  const uint16_t* B1 = reinterpret_cast<const uint16_t*>(wexp + b1_off);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int wm0 = (wave / WN) * (BM / WM);
-  const int wn0 = (wave % WN) * (BN / WN);
-
-  // A rows this thread loads: row r of the tile is A row tile.row0 + r, or, gathered,
-  // A row a_index[tile.row0 + r] / a_div (rows past the tile read row 0, never stored)
-  const uint16_t* a_row[CA];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int r = (tid + i * NT) / KC;
-    int src = tile.row0 + (r < tile.rows ? r : 0);
-    if (a_index) src = a_index[src] / a_div;
-    a_row[i] = A + static_cast<int64_t>(src) * lda;
-  }
-
-  uint4 ra[CA], rb[CB];
-
-#define MOE_LOAD_REGS(k0)                                                                     \
-  do {                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < CA; ++i) {                                          \
-      const int c = tid + i * NT;                                                             \
-      const int r = c / KC, k = (k0) + (c % KC) * 8;                                          \
-      ra[i] = make_uint4(0, 0, 0, 0);                                                         \
-      if (r < tile.rows && k < K)                                                             \
-        ra[i] = *reinterpret_cast<const uint4*>(a_row[i] + k);                               \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < CB; ++i) {                                          \
-      const int c = tid + i * NT;                                                             \
-      const int r = c / KC, k = (k0) + (c % KC) * 8;                                          \
-      const int n = n0 + (DUAL ? r % BN : r);                                                 \
-      const uint16_t* Bm = (DUAL && r >= BN) ? B1 : B0;                                       \
-      rb[i] = make_uint4(0, 0, 0, 0);                                                         \
-      if (n < N && k < K)                                                                     \
-        rb[i] = *reinterpret_cast<const uint4*>(Bm + static_cast<int64_t>(n) * K + k);        \
-    }                                                                                         \
-  } while (0)
-
-#define MOE_STORE_LDS(buf)                                                                    \
-  do {                                                                                        \
-    uint16_t* as_ = As + (buf) * BM * LDS_LD;                                                 \
-    uint16_t* bs_ = Bs + (buf) * NB * BN * LDS_LD;                                            \
-    _Pragma("unroll") for (int i = 0; i < CA; ++i) {                                          \
-      const int c = tid + i * NT;                                                             \
-      *reinterpret_cast<uint4*>(as_ + (c / KC) * LDS_LD + (c % KC) * 8) = ra[i];              \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < CB; ++i) {                                          \
-      const int c = tid + i * NT;                                                             \
-      *reinterpret_cast<uint4*>(bs_ + (c / KC) * LDS_LD + (c % KC) * 8) = rb[i];              \
-    }                                                                                         \
-  } while (0)
-
-  floatx4 acc0[TM][TN], acc1[DUAL ? TM : 1][DUAL ? TN : 1];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc0[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (DUAL) {
-#pragma unroll
-    for (int i = 0; i < (DUAL ? TM : 1); ++i)
-#pragma unroll
-      for (int j = 0; j < (DUAL ? TN : 1); ++j) acc1[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int nk = (K + BK - 1) / BK;
-  MOE_LOAD_REGS(0);
-  MOE_STORE_LDS(0);
-  __syncthreads();
-
-  const int lrow = lane & 15;        // operand row (A) / column (B) of this lane
-  const int lk = (lane >> 4) * 8;    // first of this lane's 8 K values
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) MOE_LOAD_REGS((kt + 1) * BK);
-    const uint16_t* as = As + cur * BM * LDS_LD;
-    const uint16_t* bs = Bs + cur * NB * BN * LDS_LD;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8_t a[TM], b0[TN], b1[DUAL ? TN : 1];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(as + (wm0 + i * 16 + lrow) * LDS_LD + kk + lk);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        b0[j] = *reinterpret_cast<const bf16x8_t*>(bs + (wn0 + j * 16 + lrow) * LDS_LD + kk + lk);
-        if (DUAL)
-          b1[DUAL ? j : 0] = *reinterpret_cast<const bf16x8_t*>(
-              bs + (BN + wn0 + j * 16 + lrow) * LDS_LD + kk + lk);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          acc0[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b0[j], acc0[i][j], 0, 0, 0);
-          if (DUAL)
-            acc1[DUAL ? i : 0][DUAL ? j : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a[i], b1[DUAL ? j : 0], acc1[DUAL ? i : 0][DUAL ? j : 0], 0, 0, 0);
-        }
-    }
-    if (kt + 1 < nk) MOE_STORE_LDS(cur ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds D[(lane/16)*4 + q][lane%16] of each 16x16 block
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = wm0 + i * 16 + (lane >> 4) * 4 + q;
-        const int n = n0 + wn0 + j * 16 + (lane & 15);
-        if (r >= tile.rows || n >= N) continue;
-        const int64_t o = static_cast<int64_t>(tile.row0 + r) * ldo + n;
-        if (DUAL) {
-          const float g = acc0[i][j][q];
-          const float u = acc1[DUAL ? i : 0][DUAL ? j : 0][q];
-          static_cast<uint16_t*>(out)[o] = f32_to_bf16(silu_f32(g) * u);
-        } else if (OUT_BF16) {
-          static_cast<uint16_t*>(out)[o] = f32_to_bf16(acc0[i][j][q]);
-        } else {
-          static_cast<float*>(out)[o] = acc0[i][j][q];
-        }
-      }
-}
-
-#undef MOE_LOAD_REGS
-#undef MOE_STORE_LDS
-
-template <int BM, int BN, int BK, int WM, int WN, bool DUAL, bool OUT_BF16>
-struct GemmShape {
-  static constexpr int kThreads = WM * WN * kWave;
-  static constexpr size_t kLds =
-      2 * static_cast<size_t>(BM + (DUAL ? 2 : 1) * BN) * (BK + 8) * sizeof(uint16_t);
-
-  static int launch(const uint16_t* A, int lda, const int32_t* a_index, int a_div,
-                    const char* wbase, int64_t expert_bytes,
-                    int64_t b0_off, int64_t b1_off, int N, int K, const Tile* tiles,
-                    const int32_t* n_tiles, int64_t grid_tiles, int dense_M, void* out, int ldo,
-                    hipStream_t s) {
-    auto kern = gemm_bf16_kernel<BM, BN, BK, WM, WN, DUAL, OUT_BF16>;
-    static bool configured = false;
-    if (!configured) {
-      MOE_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        static_cast<int>(kLds)));
-      configured = true;
-    }
-    if (grid_tiles <= 0) return MOE_OK;
-    dim3 grid(static_cast<unsigned>(grid_tiles), static_cast<unsigned>(ceil_div(N, BN)));
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLds, s, A, lda, a_index, a_div, wbase,
-                       expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles, dense_M, out, ldo);
-    MOE_LAUNCH_CHECK("gemm_bf16_kernel launch");
-    return MOE_OK;
-  }
-};
-
-
 // ---------------------------------------------------------------------------
-// Prefill tile GEMM: 256 x 256 block tile, 8 waves (two per SIMD), 32x32x16
-// MFMA, BK = 64, LDS double buffer (144 KB of the CU's 160 KB).
-//
-// DUAL (gate/up): the B tile holds 128 Wg rows and the same 128 Wu rows, so
-// a block produces 256 rows x 128 columns of h; each wave owns 128 rows x 32
-// columns of both g and u and applies silu(g) * u in registers.  !DUAL: the B
-// tile is 256 rows of one matrix; each wave owns 128 rows x 64 columns.
-//
-// Work order: the (m-tile, n-tile) items are cut into 8 contiguous chunks,
-// one per XCD (workgroup i runs on XCD i % 8), and inside a chunk groups of
-// kMGroup consecutive m-tiles sweep the n-tiles together, so the blocks that
-// run at the same time on one XCD share A tiles and weight panels in its L2.
+// Prefill work order: the (m-tile, n-tile) items are cut into 8 contiguous
+// chunks, one per XCD (workgroup i runs on XCD i % 8), and inside a chunk
+// groups of kMGroup consecutive m-tiles sweep the n-tiles together, so the
+// blocks that run at the same time on one XCD share A tiles and weight panels
+// in its L2.
 // ---------------------------------------------------------------------------
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -322,18 +113,37 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kXcds = 8;
 constexpr int kMGroup = 4;
 
-template <bool DUAL, bool OUT_BF16>
-__global__ __launch_bounds__(512) void gemm_big_kernel(
+// ---------------------------------------------------------------------------
+// Prefill tile GEMM, one wave per SIMD: 256 x 256 block tile, 4 waves each
+// owning a 128 x 128 quarter (4 x 4 blocks of 32x32x16 MFMA, all 256
+// accumulators per lane), BK = 64, LDS double buffer (144 KB).  Against an
+// 8-wave split into 128 x 64 quarters this reads a third less LDS per MFMA
+// (each operand fetched from LDS feeds four MFMAs), and LDS bandwidth is what
+// bounds this loop.  The loop is software-pipelined by hand:
+// the operand fragments of K step s + 1 are read from LDS while the MFMAs of
+// step s issue, and every stage's global loads are issued a full K iteration
+// before their LDS write, one chunk per MFMA, so HBM latency stays hidden with
+// a single wave per SIMD.
+//
+// DUAL (gate/up): the B tile holds 128 Wg rows and the same 128 Wu rows; wave
+// (wm, wn) owns h rows 128 wm .. +128 and columns 64 wn .. +64, i.e. B-tile
+// rows 64 wn .. +64 (gate) and 128 + 64 wn .. +64 (up).  !DUAL: wave (wm, wn)
+// owns output columns 128 wn .. +128.
+// ---------------------------------------------------------------------------
+
+template <bool DUAL, bool OUT_BF16, bool KFULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_wide_kernel(
     const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ a_index, int a_div,
     const char* __restrict__ wbase, int64_t expert_bytes,
     int64_t b0_off, int64_t b1_off, int N, int K, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, int dense_M, void* __restrict__ out, int ldo) {
-  constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+  constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
   constexpr int LDS_LD = BK + 8;
-  constexpr int KC = BK / 8;
-  constexpr int CA = BM * KC / NT;   // 4
-  constexpr int CB = BN * KC / NT;   // 4
+  constexpr int KC = BK / 8;           // 16-byte chunks per row per stage
+  constexpr int CH = BM * KC / NT;     // 8 A chunks and 8 B chunks per thread per stage
+  constexpr int RSTEP = NT / KC;       // 32: row distance between a thread's chunks
   constexpr int OUTN = DUAL ? BN / 2 : BN;
+  constexpr int STAGE = BM * LDS_LD;   // elements of one A (or B) stage buffer
 
   const int n_m = tiles ? *n_tiles : (dense_M + BM - 1) / BM;
   const int n_n = (N + OUTN - 1) / OUTN;
@@ -361,8 +171,8 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
   const int n0 = nt * OUTN;
 
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* As = smem;                       // [2][BM][LDS_LD]
-  uint16_t* Bs = smem + 2 * BM * LDS_LD;     // [2][BN][LDS_LD]
+  uint16_t* As = smem;                 // [2][BM][LDS_LD]
+  uint16_t* Bs = smem + 2 * STAGE;     // [2][BN][LDS_LD]
 
   const char* wexp = wbase + static_cast<int64_t>(tile.slot) * expert_bytes;
   const uint16_t* B0 = reinterpret_cast<const uint16_t*>(wexp + b0_off);
@@ -371,109 +181,151 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wm0 = (wave >> 2) * 128;          // 2 waves down M
-  const int wq = wave & 3;                     // 4 waves across N
+  const int wm0 = (wave >> 1) * 128;
+  const int wn = wave & 1;
 
-  // per-thread load slots (fixed over the K loop)
-  const uint16_t* a_src[CA];
-  bool a_ok[CA];
-  int a_lds[CA];
+  // Load slots: chunk i of this thread is tile row tid / KC + RSTEP * i, K chunk tid % KC.
+  // Rows past the tile and columns past N read a valid row instead (row 0 of the tile,
+  // weight row 0): their products only reach outputs that are never stored.
+  const int kc = tid % KC;
+  const int lr0 = tid / KC;
+  const uint16_t* a_src[CH];
+  const uint16_t* b_src[CH];
+  // tile row r is A row tile.row0 + r, or, gathered, A row a_index[tile.row0 + r] / a_div
+  int src[CH];
 #pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int c = tid + i * NT;
-    const int r = c / KC, kc = c % KC;
-    a_ok[i] = r < tile.rows;
-    // tile row r is A row tile.row0 + r, or, gathered, A row a_index[tile.row0 + r] / a_div
-    int src = tile.row0 + (a_ok[i] ? r : 0);
-    if (a_index) src = a_index[src] / a_div;
-    a_src[i] = A + static_cast<int64_t>(src) * lda + kc * 8;
-    a_lds[i] = r * LDS_LD + kc * 8;
+  for (int i = 0; i < CH; ++i) {
+    const int r = lr0 + RSTEP * i;
+    src[i] = tile.row0 + (r < tile.rows ? r : 0);
   }
-  const uint16_t* b_src[CB];
-  bool b_ok[CB];
-  int b_lds[CB];
+  if (a_index) {
 #pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int c = tid + i * NT;
-    const int r = c / KC, kc = c % KC;
+    for (int i = 0; i < CH; ++i) src[i] = a_index[src[i]];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) src[i] /= a_div;
+  }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int r = lr0 + RSTEP * i;
+    a_src[i] = A + static_cast<int64_t>(src[i]) * lda + kc * 8;
     const int n = n0 + (DUAL ? (r & (BN / 2 - 1)) : r);
     const uint16_t* Bm = (DUAL && r >= BN / 2) ? B1 : B0;
-    b_ok[i] = n < N;
-    b_src[i] = Bm + static_cast<int64_t>(b_ok[i] ? n : 0) * K + kc * 8;
-    b_lds[i] = r * LDS_LD + kc * 8;
+    b_src[i] = Bm + static_cast<int64_t>(n < N ? n : 0) * K + kc * 8;
+  }
+  const int st_off = lr0 * LDS_LD + kc * 8;
+
+  // operand rows of this lane inside the LDS tiles (32x32x16: row lane % 32, K (lane / 32) * 8)
+  const int lrow = lane & 31;
+  const int lk = (lane >> 5) * 8;
+  const int a_rd = (wm0 + lrow) * LDS_LD + lk;
+  int b_rd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int br = DUAL ? (j < 2 ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - 2) * 32)
+                        : wn * 128 + j * 32;
+    b_rd[j] = (br + lrow) * LDS_LD + lk;
   }
 
-  uint4 ra[CA], rb[CB];
-#define BIG_LOAD(k0)                                                              \
-  do {                                                                            \
-    _Pragma("unroll") for (int i = 0; i < CA; ++i) {                              \
-      ra[i] = make_uint4(0, 0, 0, 0);                                             \
-      if (a_ok[i] && (k0) + (((tid + i * NT) % KC) * 8) < K)                      \
-        ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + (k0));                 \
-    }                                                                             \
-    _Pragma("unroll") for (int i = 0; i < CB; ++i) {                              \
-      rb[i] = make_uint4(0, 0, 0, 0);                                             \
-      if (b_ok[i] && (k0) + (((tid + i * NT) % KC) * 8) < K)                      \
-        rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + (k0));                 \
-    }                                                                             \
-  } while (0)
-#define BIG_STORE(buf)                                                            \
-  do {                                                                            \
-    _Pragma("unroll") for (int i = 0; i < CA; ++i)                                \
-      *reinterpret_cast<uint4*>(As + (buf) * BM * LDS_LD + a_lds[i]) = ra[i];     \
-    _Pragma("unroll") for (int i = 0; i < CB; ++i)                                \
-      *reinterpret_cast<uint4*>(Bs + (buf) * BN * LDS_LD + b_lds[i]) = rb[i];     \
-  } while (0)
-
-  floatx16 acc[4][2];
+  floatx16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // operand rows of this lane inside the LDS tiles
-  const int lrow = lane & 31;
-  const int lk = (lane >> 5) * 8;
-  int brow[2];
-  if (DUAL) {
-    brow[0] = wq * 32 + lrow;
-    brow[1] = BN / 2 + wq * 32 + lrow;
-  } else {
-    brow[0] = wq * 64 + lrow;
-    brow[1] = wq * 64 + 32 + lrow;
-  }
+  uint4 ra[CH], rb[CH];                    // next stage, in flight from global memory
+  bf16x8_t pa[4], pb[4], qa[4], qb[4];     // operands of two consecutive K steps
+
+  // one global chunk load (slot t: 0-7 A, 8-15 B); past K the chunk is zero
+#define W_GLD(t, k0)                                                                   \
+  do {                                                                                 \
+    const uint16_t* src_ = ((t) < CH ? a_src[(t) % CH] : b_src[(t) % CH]) + (k0);      \
+    uint4 v_;                                                                          \
+    if (KFULL) {                                                                       \
+      v_ = *reinterpret_cast<const uint4*>(src_);                                      \
+    } else {                                                                           \
+      v_ = make_uint4(0, 0, 0, 0);                                                     \
+      if ((k0) + kc * 8 < K) v_ = *reinterpret_cast<const uint4*>(src_);               \
+    }                                                                                  \
+    if ((t) < CH) ra[(t) % CH] = v_; else rb[(t) % CH] = v_;                           \
+  } while (0)
+#define W_DSW(t, buf)                                                                  \
+  do {                                                                                 \
+    if ((t) < CH)                                                                      \
+      *reinterpret_cast<uint4*>(As + (buf) * STAGE + st_off + ((t) % CH) * RSTEP * LDS_LD) = ra[(t) % CH]; \
+    else                                                                               \
+      *reinterpret_cast<uint4*>(Bs + (buf) * STAGE + st_off + ((t) % CH) * RSTEP * LDS_LD) = rb[(t) % CH]; \
+  } while (0)
+  // one operand fragment read (slot t: 0-3 A row blocks, 4-7 B column blocks) of K step s
+#define W_DSR(RA, RB, t, buf, s)                                                       \
+  do {                                                                                 \
+    if ((t) < 4)                                                                       \
+      RA[(t) % 4] = *reinterpret_cast<const bf16x8_t*>(As + (buf) * STAGE + a_rd +     \
+                                                       ((t) % 4) * 32 * LDS_LD + (s) * 16); \
+    else                                                                               \
+      RB[(t) % 4] = *reinterpret_cast<const bf16x8_t*>(Bs + (buf) * STAGE + b_rd[(t) % 4] + (s) * 16); \
+  } while (0)
+#define W_MFMA(RA, RB, t)                                                              \
+  acc[(t) / 4][(t) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(RA[(t) / 4], RB[(t) % 4], \
+                                                                 acc[(t) / 4][(t) % 4], 0, 0, 0)
+  // One K step: 16 MFMAs on (RA, RB); between them, in issue order, the operand reads of
+  // the following step into (NA, NB), and the LDS write of each staged chunk followed by
+  // the global load that refills its registers with the stage after.
+#define W_STEP(RA, RB, NA, NB, rd_buf, rd_s, DO_RD, DO_DSW, wbuf, DO_GLD, gk0)           \
+  do {                                                                                 \
+    _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                   \
+      W_MFMA(RA, RB, t);                                                               \
+      if ((DO_RD) && t < 8) W_DSR(NA, NB, t, rd_buf, rd_s);                            \
+      if (DO_DSW) W_DSW(t, wbuf);                                                      \
+      if (DO_GLD) W_GLD(t, gk0);                                                       \
+      __builtin_amdgcn_sched_barrier(0);                                               \
+    }                                                                                  \
+  } while (0)
+  // K iteration kt computes stage kt from LDS buffer kt & 1, writes stage kt + 1 (loaded
+  // one iteration earlier) into the other buffer and loads stage kt + 2 into registers.
+  // Step 3's MFMAs run after the barrier that publishes stage kt + 1, overlapping the
+  // first operand reads from it.
+#define W_ITER(DO_DSW, DO_GLD)                                                         \
+  do {                                                                                 \
+    const int cur = kt & 1;                                                            \
+    W_STEP(pa, pb, qa, qb, cur, 1, true, false, 0, false, 0);                          \
+    W_STEP(qa, qb, pa, pb, cur, 2, true, false, 0, false, 0);                          \
+    W_STEP(pa, pb, qa, qb, cur, 3, true, DO_DSW, cur ^ 1, DO_GLD, (kt + 2) * BK);      \
+    if (DO_DSW) {                                                                      \
+      __syncthreads();                                                                 \
+      W_STEP(qa, qb, pa, pb, cur ^ 1, 0, true, false, 0, false, 0);                    \
+    } else {                                                                           \
+      W_STEP(qa, qb, pa, pb, 0, 0, false, false, 0, false, 0);                         \
+    }                                                                                  \
+  } while (0)
 
   const int nk = (K + BK - 1) / BK;
-  BIG_LOAD(0);
-  BIG_STORE(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) BIG_LOAD((kt + 1) * BK);
-    const uint16_t* as = As + cur * BM * LDS_LD;
-    const uint16_t* bs = Bs + cur * BN * LDS_LD;
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 16) {
-      bf16x8_t a[4], b[2];
+  for (int t = 0; t < 2 * CH; ++t) W_GLD(t, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(as + (wm0 + i * 32 + lrow) * LDS_LD + ks + lk);
+  for (int t = 0; t < 2 * CH; ++t) W_DSW(t, 0);
+  if (nk > 1) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(bs + brow[j] * LDS_LD + ks + lk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) BIG_STORE(cur ^ 1);
-    __syncthreads();
+    for (int t = 0; t < 2 * CH; ++t) W_GLD(t, BK);
   }
-#undef BIG_LOAD
-#undef BIG_STORE
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < 8; ++t) W_DSR(pa, pb, t, 0, 0);
+
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) W_ITER(true, true);
+  if (kt + 1 < nk) {
+    W_ITER(true, false);
+    ++kt;
+  }
+  W_ITER(false, false);
+#undef W_ITER
+#undef W_GLD
+#undef W_DSW
+#undef W_DSR
+#undef W_MFMA
+#undef W_STEP
 
   // epilogue: element q of a 32x32 block sits at row (q/4)*8 + (lane/32)*4 + q%4, column lane%32
 #pragma unroll
@@ -484,13 +336,17 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
       if (r >= tile.rows) continue;
       const int64_t orow = static_cast<int64_t>(tile.row0 + r) * ldo;
       if (DUAL) {
-        const int n = n0 + wq * 32 + lrow;
-        if (n < N)
-          static_cast<uint16_t*>(out)[orow + n] = f32_to_bf16(silu_f32(acc[i][0][q]) * acc[i][1][q]);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int n = n0 + wn * 64 + jj * 32 + lrow;
+          if (n < N)
+            static_cast<uint16_t*>(out)[orow + n] =
+                f32_to_bf16(silu_f32(acc[i][jj][q]) * acc[i][2 + jj][q]);
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wq * 64 + j * 32 + lrow;
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * 128 + j * 32 + lrow;
           if (n >= N) continue;
           if (OUT_BF16) static_cast<uint16_t*>(out)[orow + n] = f32_to_bf16(acc[i][j][q]);
           else static_cast<float*>(out)[orow + n] = acc[i][j][q];
@@ -500,7 +356,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
 }
 
 template <bool DUAL, bool OUT_BF16>
-struct GemmBig {
+struct GemmWide {
   static constexpr int BM = 256;
   static constexpr size_t kLds = 2 * static_cast<size_t>(256 + 256) * (64 + 8) * sizeof(uint16_t);
 
@@ -510,33 +366,170 @@ struct GemmBig {
                     int64_t b0_off, int64_t b1_off, int N, int K, const Tile* tiles,
                     const int32_t* n_tiles, int64_t grid_m, int dense_M, void* out, int ldo,
                     hipStream_t s) {
-    auto kern = gemm_big_kernel<DUAL, OUT_BF16>;
+    auto kern = K % 64 == 0 ? gemm_wide_kernel<DUAL, OUT_BF16, true>
+                            : gemm_wide_kernel<DUAL, OUT_BF16, false>;
     static bool configured = false;
     if (!configured) {
-      MOE_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        static_cast<int>(kLds)));
+      for (auto k : {gemm_wide_kernel<DUAL, OUT_BF16, true>, gemm_wide_kernel<DUAL, OUT_BF16, false>})
+        MOE_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          static_cast<int>(kLds)));
       configured = true;
     }
     if (grid_m <= 0) return MOE_OK;
     const int outn = DUAL ? 128 : 256;
     const int64_t items = grid_m * ceil_div(N, outn);
     const int64_t blocks = ceil_div64(items, kXcds) * kXcds;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(512), kLds, s, A, lda, a_index,
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), kLds, s, A, lda, a_index,
                        a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles, dense_M,
                        out, ldo);
-    MOE_LAUNCH_CHECK("gemm_big_kernel launch");
+    MOE_LAUNCH_CHECK("gemm_wide_kernel launch");
     return MOE_OK;
   }
 };
 
-// decode shapes: 16-row tiles, weights streamed in 128-deep K steps
-using Gemm1Decode = GemmShape<16, 64, 128, 1, 4, true, false>;
-using Gemm2Decode = GemmShape<16, 64, 128, 1, 4, false, false>;
+// ---------------------------------------------------------------------------
+// Decode tile GEMM: a tile holds at most 16 rows, so each weight element feeds
+// exactly one MFMA and the kernel is a weight stream.  No LDS and no barriers:
+// every wave streams its own weight rows straight into registers in the MFMA
+// operand layout (lane l: row l % 16, the 8 K values 8 (l / 16) .. +8 of each
+// 32-deep MFMA step), so one load instruction reads 64 contiguous bytes of
+// each of 16 rows.  K is consumed in 128-deep superblocks of four MFMA steps,
+// two superblocks in flight per wave (ping-pong register sets).
+//   DUAL: a wave owns 32 output columns (2 gate + 2 up 16-column MFMA blocks);
+//   !DUAL: 64 output columns (4 blocks).  Four waves per block.
+// ---------------------------------------------------------------------------
+
+//   NB  16-column MFMA blocks per wave (DUAL: NB / 2 gate + NB / 2 up blocks)
+//   KS  32-deep MFMA steps per register stage
+template <bool DUAL, bool KFULL, int NB, int KS>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(
+    const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ a_index, int a_div,
+    const char* __restrict__ wbase, int64_t expert_bytes, int64_t b0_off, int64_t b1_off, int N,
+    int K, const Tile* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
+    void* __restrict__ out, int ldo) {
+  constexpr int WCOLS = DUAL ? NB * 8 : NB * 16;
+  constexpr int BCOLS = 4 * WCOLS;
+  constexpr int SK = 32 * KS;  // K depth of one register stage
+  static_assert(!DUAL || NB % 2 == 0, "gate and up blocks come in pairs");
+  if (static_cast<int>(blockIdx.x) >= *n_tiles) return;
+  const Tile tile = tiles[blockIdx.x];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int c0 = blockIdx.y * BCOLS + wave * WCOLS;
+  if (c0 >= N) return;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // A row of this lane (rows past the tile read the tile's first row; never stored)
+  int src = tile.row0 + (lr < tile.rows ? lr : 0);
+  if (a_index) src = a_index[src] / a_div;
+  const uint16_t* arow = A + static_cast<int64_t>(src) * lda + lg * 8;
+  const char* wexp = wbase + static_cast<int64_t>(tile.slot) * expert_bytes;
+  const uint16_t* B0 = reinterpret_cast<const uint16_t*>(wexp + b0_off);
+  const uint16_t* B1 = reinterpret_cast<const uint16_t*>(wexp + b1_off);
+  const uint16_t* brow[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int jj = DUAL ? j % (NB / 2) : j;
+    const int n = c0 + jj * 16 + lr;
+    const uint16_t* Bm = (DUAL && j >= NB / 2) ? B1 : B0;
+    brow[j] = Bm + static_cast<int64_t>(n < N ? n : 0) * K + lg * 8;
+  }
+
+  floatx4 acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 a0[KS], b0[NB][KS], a1[KS], b1[NB][KS];
+#define STREAM_LOAD(AR, BR, k0)                                                                   \
+  do {                                                                                            \
+    _Pragma("unroll") for (int c = 0; c < KS; ++c) {                                              \
+      const bool in = KFULL || (k0) + c * 32 + lg * 8 < K;                                        \
+      AR[c] = make_uint4(0, 0, 0, 0);                                                             \
+      if (in) AR[c] = *reinterpret_cast<const uint4*>(arow + (k0) + c * 32);                      \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j) {                                            \
+        BR[j][c] = make_uint4(0, 0, 0, 0);                                                        \
+        if (in) BR[j][c] = *reinterpret_cast<const uint4*>(brow[j] + (k0) + c * 32);              \
+      }                                                                                           \
+    }                                                                                             \
+  } while (0)
+#define STREAM_MFMA(AR, BR)                                                                       \
+  do {                                                                                            \
+    _Pragma("unroll") for (int c = 0; c < KS; ++c) {                                              \
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, AR[c]);                                     \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j)                                              \
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                                         \
+            a, __builtin_bit_cast(bf16x8_t, BR[j][c]), acc[j], 0, 0, 0);                          \
+    }                                                                                             \
+  } while (0)
+
+  const int nsb = (K + SK - 1) / SK;
+  STREAM_LOAD(a0, b0, 0);
+  for (int sb = 0; sb < nsb; sb += 2) {
+    if (sb + 1 < nsb) STREAM_LOAD(a1, b1, (sb + 1) * SK);
+    STREAM_MFMA(a0, b0);
+    if (sb + 1 >= nsb) break;
+    if (sb + 2 < nsb) STREAM_LOAD(a0, b0, (sb + 2) * SK);
+    STREAM_MFMA(a1, b1);
+  }
+#undef STREAM_LOAD
+#undef STREAM_MFMA
+
+  // lane holds C[(lane / 16) * 4 + q][lane % 16] of each 16x16 block
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = lg * 4 + q;
+    if (r >= tile.rows) continue;
+    const int64_t orow = static_cast<int64_t>(tile.row0 + r) * ldo;
+    if (DUAL) {
+#pragma unroll
+      for (int jj = 0; jj < NB / 2; ++jj) {
+        const int n = c0 + jj * 16 + lr;
+        if (n < N)
+          static_cast<uint16_t*>(out)[orow + n] =
+              f32_to_bf16(silu_f32(acc[jj][q]) * acc[NB / 2 + jj][q]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = c0 + j * 16 + lr;
+        if (n < N) static_cast<float*>(out)[orow + n] = acc[j][q];
+      }
+    }
+  }
+}
+
+template <bool DUAL, int NB, int KS>
+struct GemmStream {
+  static constexpr int BM = 16;
+  static constexpr int BCOLS = 4 * (DUAL ? NB * 8 : NB * 16);
+  static int launch(const uint16_t* A, int lda, const int32_t* a_index, int a_div,
+                    const char* wbase, int64_t expert_bytes, int64_t b0_off, int64_t b1_off, int N,
+                    int K, const Tile* tiles, const int32_t* n_tiles, int64_t grid_tiles, void* out,
+                    int ldo, hipStream_t s) {
+    if (grid_tiles <= 0) return MOE_OK;
+    dim3 grid(static_cast<unsigned>(grid_tiles), static_cast<unsigned>(ceil_div(N, BCOLS)));
+    if (K % (32 * KS) == 0)
+      hipLaunchKernelGGL((gemm_stream_kernel<DUAL, true, NB, KS>), grid, dim3(256), 0, s, A, lda,
+                         a_index, a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles,
+                         out, ldo);
+    else
+      hipLaunchKernelGGL((gemm_stream_kernel<DUAL, false, NB, KS>), grid, dim3(256), 0, s, A, lda,
+                         a_index, a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles,
+                         out, ldo);
+    MOE_LAUNCH_CHECK("gemm_stream_kernel launch");
+    return MOE_OK;
+  }
+};
+
+// decode shapes: gate/up with 2 + 2 blocks per wave, down with 4, 128-deep stages
+using Gemm1Stream = GemmStream<true, 4, 4>;
+using Gemm2Stream = GemmStream<false, 4, 4>;
+
 // prefill shapes: 128-row tiles
-using Gemm1Prefill = GemmBig<true, false>;
-using Gemm2Prefill = GemmBig<false, false>;
-using DenseBf16 = GemmBig<false, true>;
+using Gemm1Prefill = GemmWide<true, false>;
+using Gemm2Prefill = GemmWide<false, false>;
+using DenseBf16 = GemmWide<false, true>;
 
 // ---------------------------------------------------------------------------
 // f32 path
@@ -670,7 +663,7 @@ int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
   Tile* tiles = reinterpret_cast<Tile*>(wsb + L.tiles_off);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(wsb + L.count_off);
   const bool decode = static_cast<int64_t>(R) <= 4 * static_cast<int64_t>(E);
-  const int BM = decode ? 16 : GemmBig<true, false>::BM;
+  const int BM = decode ? 16 : Gemm1Prefill::BM;
   const int64_t grid_tiles = ceil_div64(R, BM) + std::min(E, R);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(MOE_MAX_E), 0, s, offsets, E, e_begin, e_end, BM,
                      w->slot_of, tiles, n_tiles, status);
@@ -681,11 +674,11 @@ int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   int rc;
   if (decode) {
-    rc = Gemm1Decode::launch(xp, H, a_index, a_div, wbase, eb, 0, HI2, I, H, tiles, n_tiles,
-                             grid_tiles, 0, h, I, s);
+    rc = Gemm1Stream::launch(xp, H, a_index, a_div, wbase, eb, 0, HI2, I, H, tiles, n_tiles,
+                                  grid_tiles, h, I, s);
     if (rc) return rc;
-    rc = Gemm2Decode::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
-                             grid_tiles, 0, y_perm, H, s);
+    rc = Gemm2Stream::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
+                                   grid_tiles, y_perm, H, s);
   } else {
     rc = Gemm1Prefill::launch(xp, H, a_index, a_div, wbase, eb, 0, HI2, I, H, tiles, n_tiles,
                               grid_tiles, 0, h, I, s);

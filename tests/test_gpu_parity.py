@@ -52,6 +52,9 @@ def test_tiny_fp32_layer():
     (1, 64, 32, 5, 2, 1, None),           # a single token
     (64, 256, 512, 8, 1, 4, None),        # k = 1
     (40, 96, 40, 70, 8, 20, 1.1),         # E above one wave, skew
+    (16, 136, 72, 37, 3, 9, None),        # decode tiles: K and N tails (K % 128, N % 32 != 0)
+    (24, 256, 512, 64, 8, 16, None),      # decode tiles, full 128-deep K steps
+    (12, 1024, 200, 40, 6, 10, 1.1),      # decode tiles, skew, K = 1024
 ])
 def test_small_bf16_layers(T, H, I, E, k, n_local, zipf):
     cfg = synth.MoEConfig(f"bf16_T{T}_H{H}_I{I}_E{E}_k{k}", T=T, H=H, I=I, E=E, k=k, dtype="bf16",
