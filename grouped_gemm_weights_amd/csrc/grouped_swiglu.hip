@@ -101,11 +101,12 @@ __global__ __launch_bounds__(MOE_MAX_E) void plan_kernel(const int32_t* __restri
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 // ---------------------------------------------------------------------------
-// Prefill work order: the (m-tile, n-tile) items are cut into 8 contiguous
-// chunks, one per XCD (workgroup i runs on XCD i % 8), and inside a chunk
-// groups of kMGroup consecutive m-tiles sweep the n-tiles together, so the
-// blocks that run at the same time on one XCD share A tiles and weight panels
-// in its L2.
+// Prefill work order: groups of kMGroup consecutive m-tiles sweep all n-tiles
+// together on one XCD (workgroup i runs on XCD i % 8), so the blocks that run
+// at the same time there share A tiles and weight panels in its L2; groups go
+// round-robin over the XCDs, which spreads hot and light experts evenly (a
+// split into 8 contiguous ranges left one XCD 17 % over the mean under Zipf
+// routing).
 // ---------------------------------------------------------------------------
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -114,22 +115,269 @@ constexpr int kXcds = 8;
 constexpr int kMGroup = 4;
 
 // ---------------------------------------------------------------------------
-// Prefill tile GEMM, one wave per SIMD: 256 x 256 block tile, 4 waves each
-// owning a 128 x 128 quarter (4 x 4 blocks of 32x32x16 MFMA, all 256
-// accumulators per lane), BK = 64, LDS double buffer (144 KB).  Against an
-// 8-wave split into 128 x 64 quarters this reads a third less LDS per MFMA
-// (each operand fetched from LDS feeds four MFMAs), and LDS bandwidth is what
-// bounds this loop.  The loop is software-pipelined by hand:
-// the operand fragments of K step s + 1 are read from LDS while the MFMAs of
-// step s issue, and every stage's global loads are issued a full K iteration
-// before their LDS write, one chunk per MFMA, so HBM latency stays hidden with
-// a single wave per SIMD.
+// Prefill tile GEMM, one wave per SIMD: 256 x 256 block tile, 4 waves, 32x32x16
+// MFMA, BK = 64, LDS double buffer (144 KB).
 //
-// DUAL (gate/up): the B tile holds 128 Wg rows and the same 128 Wu rows; wave
-// (wm, wn) owns h rows 128 wm .. +128 and columns 64 wn .. +64, i.e. B-tile
-// rows 64 wn .. +64 (gate) and 128 + 64 wn .. +64 (up).  !DUAL: wave (wm, wn)
-// owns output columns 128 wn .. +128.
+// Full tiles (more than 192 rows): each wave owns a 128 x 128 quarter (4 x 4
+// MFMA blocks, all 256 accumulators per lane).  Against an 8-wave split into
+// 128 x 64 quarters this reads a third less LDS per MFMA (each operand fetched
+// from LDS feeds four MFMAs), and LDS bandwidth is what bounds this loop.
+// Partial tiles (at most MI * 32 rows, MI = 2, 4 or 6): the waves split the
+// columns instead and each owns all MI * 32 rows x 64 columns, so the MFMA work
+// of the tile shrinks with its row count rather than idling whole SIMDs.  An
+// expert's last tile is usually partial (8K-token Zipf routing: 38 % of the
+// tile rows would be padding), as is every tile of a 4096-token layer.
+//
+// The loop is software-pipelined by hand: the operand fragments of K step
+// s + 1 are read from LDS while the MFMAs of step s issue, and every stage's
+// global loads are issued two K iterations before their LDS write (a two-slot
+// register ring), one chunk per MFMA slot, so HBM latency stays hidden with a
+// single wave per SIMD even when a partial tile's iterations are short.
+//
+// DUAL (gate/up): the B tile holds 128 Wg rows and the same 128 Wu rows.  Full
+// tiles: wave (wm, wn) owns h rows 128 wm .. +128 and columns 64 wn .. +64,
+// i.e. B-tile rows 64 wn .. +64 (gate) and 128 + 64 wn .. +64 (up).  Partial
+// tiles: wave w owns h columns 32 w .. +32 (gate rows 32 w, up rows 128 + 32 w).
+// !DUAL: full tiles, wave (wm, wn) owns output columns 128 wn .. +128; partial
+// tiles, wave w owns columns 64 w .. +64.
 // ---------------------------------------------------------------------------
+
+constexpr int kWideBM = 256, kWideBN = 256, kWideBK = 64, kWideLd = kWideBK + 8;
+
+// MI = 0: full tile; MI > 0: partial tile of at most MI * 32 rows
+template <bool DUAL, bool OUT_BF16, bool KFULL, int MI>
+__device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16_t* __restrict__ A,
+                                          int lda, const int32_t* __restrict__ a_index, int a_div,
+                                          const uint16_t* __restrict__ B0,
+                                          const uint16_t* __restrict__ B1, int N, int K,
+                                          void* __restrict__ out, int ldo, uint16_t* smem) {
+  constexpr int BN = kWideBN, BK = kWideBK, NT = 256;
+  constexpr int LDS_LD = kWideLd;
+  constexpr int KC = BK / 8;            // 16-byte chunks per row per stage
+  constexpr int RSTEP = NT / KC;        // 32: row distance between a thread's chunks
+  constexpr int CHB = BN / RSTEP;       // 8 B chunks per thread per stage
+  constexpr int CHA = MI ? MI : 8;      // A chunks per thread per stage (rows the tile can have)
+  constexpr int MW = MI ? MI : 4;       // 32-row MFMA blocks per wave
+  constexpr int NJ = MI ? 2 : 4;        // 32-column MFMA blocks per wave
+  constexpr int NMF = MW * NJ;          // MFMAs per 16-deep K step
+  constexpr int NRD = MW + NJ;          // operand fragments per K step
+  constexpr int NLD = CHA + CHB;        // staged chunks per stage
+  constexpr int NS = NMF > NLD ? NMF : NLD;
+  constexpr int STAGE = kWideBM * LDS_LD;  // elements of one A (or B) stage buffer
+
+  uint16_t* As = smem;                  // [2][BM][LDS_LD]
+  uint16_t* Bs = smem + 2 * STAGE;      // [2][BN][LDS_LD]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm0 = MI ? 0 : (wave >> 1) * 128;
+  const int wn = wave & 1;
+
+  // Load slots: chunk i of this thread is tile row tid / KC + RSTEP * i, K chunk tid % KC.
+  // Rows past the tile and columns past N read a valid row instead (row 0 of the tile,
+  // weight row 0): their products only reach outputs that are never stored.
+  const int kc = tid % KC;
+  const int lr0 = tid / KC;
+  // A chunks: 32-bit byte offsets from a wave-uniform base (the tile's first row, or the
+  // start of x when rows are gathered; the host keeps gathered offsets below 2^32)
+  const char* a_base = reinterpret_cast<const char*>(
+      a_index ? A : A + static_cast<int64_t>(tile.row0) * lda);
+  uint32_t a_off[CHA];
+  uint32_t b_off[CHB];                  // element offsets into B0 (B1 for DUAL chunks >= CHB / 2)
+  // tile row r is A row tile.row0 + r, or, gathered, A row a_index[tile.row0 + r] / a_div
+  int src[CHA];
+#pragma unroll
+  for (int i = 0; i < CHA; ++i) {
+    const int r = lr0 + RSTEP * i;
+    src[i] = tile.row0 + (r < tile.rows ? r : 0);
+  }
+  if (a_index) {
+#pragma unroll
+    for (int i = 0; i < CHA; ++i) src[i] = a_index[src[i]];
+#pragma unroll
+    for (int i = 0; i < CHA; ++i) src[i] /= a_div;
+  }
+#pragma unroll
+  for (int i = 0; i < CHA; ++i)
+    a_off[i] = static_cast<uint32_t>(a_index ? src[i] : src[i] - tile.row0) *
+                   static_cast<uint32_t>(lda) * 2u + kc * 16u;
+#pragma unroll
+  for (int i = 0; i < CHB; ++i) {
+    const int r = lr0 + RSTEP * i;
+    const int n = n0 + (DUAL ? (r & (BN / 2 - 1)) : r);
+    b_off[i] = static_cast<uint32_t>(n < N ? n : 0) * static_cast<uint32_t>(K) + kc * 8;
+  }
+  const int st_off = lr0 * LDS_LD + kc * 8;
+
+  // operand rows of this lane inside the LDS tiles (32x32x16: row lane % 32, K (lane / 32) * 8)
+  const int lrow = lane & 31;
+  const int lk = (lane >> 5) * 8;
+  const int a_rd = (wm0 + lrow) * LDS_LD + lk;
+  int b_rd[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    int br;
+    if (MI) br = DUAL ? (j == 0 ? wave * 32 : BN / 2 + wave * 32) : wave * 64 + j * 32;
+    else br = DUAL ? (j < 2 ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - 2) * 32) : wn * 128 + j * 32;
+    b_rd[j] = (br + lrow) * LDS_LD + lk;
+  }
+
+  floatx16 acc[MW][NJ];
+#pragma unroll
+  for (int i = 0; i < MW; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // stages in flight from global memory: two for tiles of at most 64 rows (their short K
+  // iterations would not cover the latency of one), else one (no registers left for more)
+  constexpr int RING = (MI == 2 || MI == 0) ? 2 : 1;
+  uint4 ra[RING][CHA], rb[RING][CHB];
+  bf16x8_t pa[MW], pb[NJ], qa[MW], qb[NJ]; // operands of two consecutive K steps
+
+  // one global chunk load into ring slot rs (chunk t: A chunks first, then B); past K
+  // the chunk is zero
+#define W_GLD(t, k0, rs)                                                               \
+  do {                                                                                 \
+    const uint16_t* src_ = (t) < CHA ? reinterpret_cast<const uint16_t*>(              \
+                                           a_base + (a_off[(t) % CHA] + 2u * (k0)))    \
+                         : ((DUAL && ((t) - CHA) % CHB >= CHB / 2) ? B1 : B0) +        \
+                               (b_off[((t) - CHA) % CHB] + (k0));                      \
+    uint4 v_;                                                                          \
+    if (KFULL) {                                                                       \
+      v_ = *reinterpret_cast<const uint4*>(src_);                                      \
+    } else {                                                                           \
+      v_ = make_uint4(0, 0, 0, 0);                                                     \
+      if ((k0) + kc * 8 < K) v_ = *reinterpret_cast<const uint4*>(src_);               \
+    }                                                                                  \
+    if ((t) < CHA) ra[rs][(t) % CHA] = v_; else rb[rs][((t) - CHA) % CHB] = v_;        \
+  } while (0)
+#define W_DSW(t, buf, rs)                                                              \
+  do {                                                                                 \
+    if ((t) < CHA)                                                                     \
+      *reinterpret_cast<uint4*>(As + (buf) * STAGE + st_off + ((t) % CHA) * RSTEP * LDS_LD) = \
+          ra[rs][(t) % CHA];                                                           \
+    else                                                                               \
+      *reinterpret_cast<uint4*>(Bs + (buf) * STAGE + st_off +                          \
+                                (((t) - CHA) % CHB) * RSTEP * LDS_LD) = rb[rs][((t) - CHA) % CHB]; \
+  } while (0)
+  // one operand fragment read (slot t: A row blocks first, then B column blocks) of K step s
+#define W_DSR(RA, RB, t, buf, s)                                                       \
+  do {                                                                                 \
+    if ((t) < MW)                                                                      \
+      RA[(t) % MW] = *reinterpret_cast<const bf16x8_t*>(As + (buf) * STAGE + a_rd +    \
+                                                        ((t) % MW) * 32 * LDS_LD + (s) * 16); \
+    else                                                                               \
+      RB[((t) - MW) % NJ] = *reinterpret_cast<const bf16x8_t*>(                        \
+          Bs + (buf) * STAGE + b_rd[((t) - MW) % NJ] + (s) * 16);                      \
+  } while (0)
+#define W_MFMA(RA, RB, t)                                                              \
+  acc[(t) / NJ][(t) % NJ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                   \
+      RA[(t) / NJ], RB[(t) % NJ], acc[(t) / NJ][(t) % NJ], 0, 0, 0)
+  // One K step: the MFMAs on (RA, RB); between them, in issue order, the operand reads of
+  // the following step into (NA, NB), and the LDS write of each staged chunk of ring slot
+  // rs followed by the global load that refills it.
+#define W_STEP(RA, RB, NA, NB, rd_buf, rd_s, DO_RD, DO_IO, wbuf, gk0, rs)                \
+  do {                                                                                 \
+    _Pragma("unroll") for (int t = 0; t < NS; ++t) {                                   \
+      if (t < NMF) W_MFMA(RA, RB, t);                                                  \
+      if ((DO_RD) && t < NRD) W_DSR(NA, NB, t, rd_buf, rd_s);                          \
+      if ((DO_IO) && t < NLD) {                                                        \
+        W_DSW(t, wbuf, rs);                                                            \
+        W_GLD(t, gk0, rs);                                                             \
+      }                                                                                \
+      __builtin_amdgcn_sched_barrier(0);                                               \
+    }                                                                                  \
+  } while (0)
+  // K iteration kt computes stage kt from LDS buffer kt & 1.  Stage s >= 1 waits in ring
+  // slot s % RING from its global load, issued RING iterations ahead, until iteration
+  // s - 1 writes it to LDS buffer s & 1 and reuses the slot for stage s + RING (past the
+  // last stage the load repeats the last stage and is never used).  Step 3's MFMAs run
+  // after the barrier that publishes stage kt + 1, overlapping the first operand reads.
+#define W_ITER(rs)                                                                     \
+  do {                                                                                 \
+    const int cur = kt & 1;                                                            \
+    W_STEP(pa, pb, qa, qb, cur, 1, true, false, 0, 0, 0);                              \
+    W_STEP(qa, qb, pa, pb, cur, 2, true, false, 0, 0, 0);                              \
+    W_STEP(pa, pb, qa, qb, cur, 3, true, true, cur ^ 1, min(kt + 1 + RING, nk - 1) * BK, rs); \
+    __syncthreads();                                                                   \
+    W_STEP(qa, qb, pa, pb, cur ^ 1, 0, true, false, 0, 0, 0);                          \
+  } while (0)
+
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int t = 0; t < NLD; ++t) W_GLD(t, 0, 0);
+#pragma unroll
+  for (int t = 0; t < NLD; ++t) W_DSW(t, 0, 0);
+#pragma unroll
+  for (int t = 0; t < NLD; ++t) W_GLD(t, min(1, nk - 1) * BK, 1 % RING);
+  if (RING > 1) {
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) W_GLD(t, min(2, nk - 1) * BK, 0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NRD; ++t) W_DSR(pa, pb, t, 0, 0);
+
+  int kt = 0;
+  if (RING == 1) {
+    for (; kt + 1 < nk; ++kt) W_ITER(0);
+  } else {
+    while (kt + 2 < nk) {
+      W_ITER(1 % RING);
+      ++kt;
+      W_ITER(0);
+      ++kt;
+    }
+    if (kt + 1 < nk) {
+      W_ITER(1 % RING);
+      ++kt;
+    }
+  }
+  // last stage: no LDS writes or loads left
+  {
+    const int cur = kt & 1;
+    W_STEP(pa, pb, qa, qb, cur, 1, true, false, 0, 0, 0);
+    W_STEP(qa, qb, pa, pb, cur, 2, true, false, 0, 0, 0);
+    W_STEP(pa, pb, qa, qb, cur, 3, true, false, 0, 0, 0);
+    W_STEP(qa, qb, pa, pb, 0, 0, false, false, 0, 0, 0);
+  }
+#undef W_ITER
+#undef W_GLD
+#undef W_DSW
+#undef W_DSR
+#undef W_MFMA
+#undef W_STEP
+
+  // epilogue: element q of a 32x32 block sits at row (q/4)*8 + (lane/32)*4 + q%4, column lane%32
+#pragma unroll
+  for (int i = 0; i < MW; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = wm0 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+      if (r >= tile.rows) continue;
+      const int64_t orow = static_cast<int64_t>(tile.row0 + r) * ldo;
+      if (DUAL) {
+#pragma unroll
+        for (int jj = 0; jj < NJ / 2; ++jj) {
+          const int n = n0 + (MI ? wave * 32 : wn * 64 + jj * 32) + lrow;
+          if (n < N)
+            static_cast<uint16_t*>(out)[orow + n] =
+                f32_to_bf16(silu_f32(acc[i][jj][q]) * acc[i][NJ / 2 + jj][q]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int n = n0 + (MI ? wave * 64 : wn * 128) + j * 32 + lrow;
+          if (n >= N) continue;
+          if (OUT_BF16) static_cast<uint16_t*>(out)[orow + n] = f32_to_bf16(acc[i][j][q]);
+          else static_cast<float*>(out)[orow + n] = acc[i][j][q];
+        }
+      }
+    }
+}
 
 template <bool DUAL, bool OUT_BF16, bool KFULL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_wide_kernel(
@@ -137,25 +385,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const char* __restrict__ wbase, int64_t expert_bytes,
     int64_t b0_off, int64_t b1_off, int N, int K, const Tile* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, int dense_M, void* __restrict__ out, int ldo) {
-  constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
-  constexpr int LDS_LD = BK + 8;
-  constexpr int KC = BK / 8;           // 16-byte chunks per row per stage
-  constexpr int CH = BM * KC / NT;     // 8 A chunks and 8 B chunks per thread per stage
-  constexpr int RSTEP = NT / KC;       // 32: row distance between a thread's chunks
-  constexpr int OUTN = DUAL ? BN / 2 : BN;
-  constexpr int STAGE = BM * LDS_LD;   // elements of one A (or B) stage buffer
+  constexpr int BM = kWideBM;
+  constexpr int OUTN = DUAL ? kWideBN / 2 : kWideBN;
 
   const int n_m = tiles ? *n_tiles : (dense_M + BM - 1) / BM;
   const int n_n = (N + OUTN - 1) / OUTN;
   const int total = n_m * n_n;
-  const int chunk = (total + kXcds - 1) / kXcds;
-  const int local = blockIdx.x / kXcds;
-  if (local >= chunk) return;
-  const int w = (blockIdx.x % kXcds) * chunk + local;
-  if (w >= total) return;
-  const int g = w / (n_n * kMGroup);
+  const int per_group = n_n * kMGroup;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int g = (local / per_group) * kXcds + xcd;
+  if (g * kMGroup >= n_m) return;
   const int gsize = min(kMGroup, n_m - g * kMGroup);
-  const int rem = w - g * (n_n * kMGroup);
+  const int rem = local % per_group;
+  if (rem >= gsize * n_n) return;
   const int nt = rem / gsize;
   const int mt = g * kMGroup + rem % gsize;
 
@@ -171,194 +413,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int n0 = nt * OUTN;
 
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* As = smem;                 // [2][BM][LDS_LD]
-  uint16_t* Bs = smem + 2 * STAGE;     // [2][BN][LDS_LD]
-
   const char* wexp = wbase + static_cast<int64_t>(tile.slot) * expert_bytes;
   const uint16_t* B0 = reinterpret_cast<const uint16_t*>(wexp + b0_off);
   const uint16_t* B1 = reinterpret_cast<const uint16_t*>(wexp + b1_off);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int wm0 = (wave >> 1) * 128;
-  const int wn = wave & 1;
-
-  // Load slots: chunk i of this thread is tile row tid / KC + RSTEP * i, K chunk tid % KC.
-  // Rows past the tile and columns past N read a valid row instead (row 0 of the tile,
-  // weight row 0): their products only reach outputs that are never stored.
-  const int kc = tid % KC;
-  const int lr0 = tid / KC;
-  const uint16_t* a_src[CH];
-  const uint16_t* b_src[CH];
-  // tile row r is A row tile.row0 + r, or, gathered, A row a_index[tile.row0 + r] / a_div
-  int src[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int r = lr0 + RSTEP * i;
-    src[i] = tile.row0 + (r < tile.rows ? r : 0);
-  }
-  if (a_index) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) src[i] = a_index[src[i]];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) src[i] /= a_div;
-  }
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int r = lr0 + RSTEP * i;
-    a_src[i] = A + static_cast<int64_t>(src[i]) * lda + kc * 8;
-    const int n = n0 + (DUAL ? (r & (BN / 2 - 1)) : r);
-    const uint16_t* Bm = (DUAL && r >= BN / 2) ? B1 : B0;
-    b_src[i] = Bm + static_cast<int64_t>(n < N ? n : 0) * K + kc * 8;
-  }
-  const int st_off = lr0 * LDS_LD + kc * 8;
-
-  // operand rows of this lane inside the LDS tiles (32x32x16: row lane % 32, K (lane / 32) * 8)
-  const int lrow = lane & 31;
-  const int lk = (lane >> 5) * 8;
-  const int a_rd = (wm0 + lrow) * LDS_LD + lk;
-  int b_rd[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int br = DUAL ? (j < 2 ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - 2) * 32)
-                        : wn * 128 + j * 32;
-    b_rd[j] = (br + lrow) * LDS_LD + lk;
-  }
-
-  floatx16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-  uint4 ra[CH], rb[CH];                    // next stage, in flight from global memory
-  bf16x8_t pa[4], pb[4], qa[4], qb[4];     // operands of two consecutive K steps
-
-  // one global chunk load (slot t: 0-7 A, 8-15 B); past K the chunk is zero
-#define W_GLD(t, k0)                                                                   \
-  do {                                                                                 \
-    const uint16_t* src_ = ((t) < CH ? a_src[(t) % CH] : b_src[(t) % CH]) + (k0);      \
-    uint4 v_;                                                                          \
-    if (KFULL) {                                                                       \
-      v_ = *reinterpret_cast<const uint4*>(src_);                                      \
-    } else {                                                                           \
-      v_ = make_uint4(0, 0, 0, 0);                                                     \
-      if ((k0) + kc * 8 < K) v_ = *reinterpret_cast<const uint4*>(src_);               \
-    }                                                                                  \
-    if ((t) < CH) ra[(t) % CH] = v_; else rb[(t) % CH] = v_;                           \
-  } while (0)
-#define W_DSW(t, buf)                                                                  \
-  do {                                                                                 \
-    if ((t) < CH)                                                                      \
-      *reinterpret_cast<uint4*>(As + (buf) * STAGE + st_off + ((t) % CH) * RSTEP * LDS_LD) = ra[(t) % CH]; \
-    else                                                                               \
-      *reinterpret_cast<uint4*>(Bs + (buf) * STAGE + st_off + ((t) % CH) * RSTEP * LDS_LD) = rb[(t) % CH]; \
-  } while (0)
-  // one operand fragment read (slot t: 0-3 A row blocks, 4-7 B column blocks) of K step s
-#define W_DSR(RA, RB, t, buf, s)                                                       \
-  do {                                                                                 \
-    if ((t) < 4)                                                                       \
-      RA[(t) % 4] = *reinterpret_cast<const bf16x8_t*>(As + (buf) * STAGE + a_rd +     \
-                                                       ((t) % 4) * 32 * LDS_LD + (s) * 16); \
-    else                                                                               \
-      RB[(t) % 4] = *reinterpret_cast<const bf16x8_t*>(Bs + (buf) * STAGE + b_rd[(t) % 4] + (s) * 16); \
-  } while (0)
-#define W_MFMA(RA, RB, t)                                                              \
-  acc[(t) / 4][(t) % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(RA[(t) / 4], RB[(t) % 4], \
-                                                                 acc[(t) / 4][(t) % 4], 0, 0, 0)
-  // One K step: 16 MFMAs on (RA, RB); between them, in issue order, the operand reads of
-  // the following step into (NA, NB), and the LDS write of each staged chunk followed by
-  // the global load that refills its registers with the stage after.
-#define W_STEP(RA, RB, NA, NB, rd_buf, rd_s, DO_RD, DO_DSW, wbuf, DO_GLD, gk0)           \
-  do {                                                                                 \
-    _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                   \
-      W_MFMA(RA, RB, t);                                                               \
-      if ((DO_RD) && t < 8) W_DSR(NA, NB, t, rd_buf, rd_s);                            \
-      if (DO_DSW) W_DSW(t, wbuf);                                                      \
-      if (DO_GLD) W_GLD(t, gk0);                                                       \
-      __builtin_amdgcn_sched_barrier(0);                                               \
-    }                                                                                  \
-  } while (0)
-  // K iteration kt computes stage kt from LDS buffer kt & 1, writes stage kt + 1 (loaded
-  // one iteration earlier) into the other buffer and loads stage kt + 2 into registers.
-  // Step 3's MFMAs run after the barrier that publishes stage kt + 1, overlapping the
-  // first operand reads from it.
-#define W_ITER(DO_DSW, DO_GLD)                                                         \
-  do {                                                                                 \
-    const int cur = kt & 1;                                                            \
-    W_STEP(pa, pb, qa, qb, cur, 1, true, false, 0, false, 0);                          \
-    W_STEP(qa, qb, pa, pb, cur, 2, true, false, 0, false, 0);                          \
-    W_STEP(pa, pb, qa, qb, cur, 3, true, DO_DSW, cur ^ 1, DO_GLD, (kt + 2) * BK);      \
-    if (DO_DSW) {                                                                      \
-      __syncthreads();                                                                 \
-      W_STEP(qa, qb, pa, pb, cur ^ 1, 0, true, false, 0, false, 0);                    \
-    } else {                                                                           \
-      W_STEP(qa, qb, pa, pb, 0, 0, false, false, 0, false, 0);                         \
-    }                                                                                  \
-  } while (0)
-
-  const int nk = (K + BK - 1) / BK;
-#pragma unroll
-  for (int t = 0; t < 2 * CH; ++t) W_GLD(t, 0);
-#pragma unroll
-  for (int t = 0; t < 2 * CH; ++t) W_DSW(t, 0);
-  if (nk > 1) {
-#pragma unroll
-    for (int t = 0; t < 2 * CH; ++t) W_GLD(t, BK);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < 8; ++t) W_DSR(pa, pb, t, 0, 0);
-
-  int kt = 0;
-  for (; kt + 2 < nk; ++kt) W_ITER(true, true);
-  if (kt + 1 < nk) {
-    W_ITER(true, false);
-    ++kt;
-  }
-  W_ITER(false, false);
-#undef W_ITER
-#undef W_GLD
-#undef W_DSW
-#undef W_DSR
-#undef W_MFMA
-#undef W_STEP
-
-  // epilogue: element q of a 32x32 block sits at row (q/4)*8 + (lane/32)*4 + q%4, column lane%32
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = wm0 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-      if (r >= tile.rows) continue;
-      const int64_t orow = static_cast<int64_t>(tile.row0 + r) * ldo;
-      if (DUAL) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int n = n0 + wn * 64 + jj * 32 + lrow;
-          if (n < N)
-            static_cast<uint16_t*>(out)[orow + n] =
-                f32_to_bf16(silu_f32(acc[i][jj][q]) * acc[i][2 + jj][q]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 128 + j * 32 + lrow;
-          if (n >= N) continue;
-          if (OUT_BF16) static_cast<uint16_t*>(out)[orow + n] = f32_to_bf16(acc[i][j][q]);
-          else static_cast<float*>(out)[orow + n] = acc[i][j][q];
-        }
-      }
-    }
+  if (tile.rows > 192)
+    wide_tile<DUAL, OUT_BF16, KFULL, 0>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem);
+  else if (tile.rows > 128)
+    wide_tile<DUAL, OUT_BF16, KFULL, 6>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem);
+  else if (tile.rows > 64)
+    wide_tile<DUAL, OUT_BF16, KFULL, 4>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem);
+  else
+    wide_tile<DUAL, OUT_BF16, KFULL, 2>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem);
 }
 
 template <bool DUAL, bool OUT_BF16>
 struct GemmWide {
-  static constexpr int BM = 256;
-  static constexpr size_t kLds = 2 * static_cast<size_t>(256 + 256) * (64 + 8) * sizeof(uint16_t);
+  static constexpr int BM = kWideBM;
+  static constexpr size_t kLds =
+      2 * static_cast<size_t>(kWideBM + kWideBN) * kWideLd * sizeof(uint16_t);
 
   // grid_m: upper bound on the number of m-tiles
   static int launch(const uint16_t* A, int lda, const int32_t* a_index, int a_div,
@@ -378,8 +450,8 @@ struct GemmWide {
     }
     if (grid_m <= 0) return MOE_OK;
     const int outn = DUAL ? 128 : 256;
-    const int64_t items = grid_m * ceil_div(N, outn);
-    const int64_t blocks = ceil_div64(items, kXcds) * kXcds;
+    const int64_t groups = ceil_div64(grid_m, kMGroup);
+    const int64_t blocks = ceil_div64(groups, kXcds) * kXcds * kMGroup * ceil_div(N, outn);
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), kLds, s, A, lda, a_index,
                        a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles, dense_M,
                        out, ldo);
@@ -633,6 +705,9 @@ int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
     return fail(MOE_ERR_ARG, "moe_grouped_swiglu: merged buffer holds %lld-byte blocks for E=%d, "
                 "expected %lld for E=%d", static_cast<long long>(w->expert_bytes), w->n_experts,
                 static_cast<long long>(eb), E);
+  if (static_cast<int64_t>(H) * I >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_swiglu: H*I=%lld is 2^31 or more",
+                static_cast<long long>(H) * I);
   if (dtype == MOE_BF16 && (H % 8 != 0 || I % 8 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_swiglu: H=%d and I=%d must be multiples of 8", H, I);
   const SwigluWs L = swiglu_ws(R, E, I, dtype);
@@ -663,6 +738,10 @@ int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
   Tile* tiles = reinterpret_cast<Tile*>(wsb + L.tiles_off);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(wsb + L.count_off);
   const bool decode = static_cast<int64_t>(R) <= 4 * static_cast<int64_t>(E);
+  if (!decode && a_index &&
+      (static_cast<int64_t>(R) / a_div + 1) * H * 2 >= (int64_t{1} << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_swiglu_gathered: x of %lld rows x %d is 4 GiB "
+                "or more", static_cast<long long>(R) / a_div + 1, H);
   const int BM = decode ? 16 : Gemm1Prefill::BM;
   const int64_t grid_tiles = ceil_div64(R, BM) + std::min(E, R);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(MOE_MAX_E), 0, s, offsets, E, e_begin, e_end, BM,
@@ -727,6 +806,9 @@ extern "C" int moe_dense_gemm(const void* x, const void* w, int M, int N, int K,
   if (M < 0 || N < 1 || K < 1) return fail(MOE_ERR_ARG, "moe_dense_gemm: bad sizes M=%d N=%d K=%d", M, N, K);
   if (N % 8 != 0 || K % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "moe_dense_gemm: N=%d and K=%d must be multiples of 8", N, K);
+  if (static_cast<int64_t>(N) * K >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_dense_gemm: N*K=%lld is 2^31 or more",
+                static_cast<long long>(N) * K);
   if (M == 0) return MOE_OK;
   if (!x || !w || !out) return fail(MOE_ERR_ARG, "moe_dense_gemm: null pointer");
   return DenseBf16::launch(static_cast<const uint16_t*>(x), K, nullptr, 1, static_cast<const char*>(w), 0, 0, 0,
