@@ -60,6 +60,11 @@ def parse():
     p.add_argument("--calibrate", action="store_true",
                    help="run only a plain streaming kernel of known size (moe_residual_add over "
                         "1 GiB elements), the reference for scaling the HBM byte counters")
+    p.add_argument("--write-traffic", metavar="PROF_DIR",
+                   help="no GPU work: turn rocprofv3 FETCH_SIZE / WRITE_SIZE csv runs under "
+                        "PROF_DIR (fetch_<config>, write_<config>, cal_fetch, cal_write) for the "
+                        "configs given with --traffic-configs into profiles/grouped_swiglu_traffic.json")
+    p.add_argument("--traffic-configs", default="r1_decode_t64")
     return p.parse_args()
 
 
@@ -189,22 +194,91 @@ def calibrate():
             "write_bytes_per_launch": 2 * n}
 
 
-def traffic_from_profiles(kernel_file):
-    """HBM bytes per moe_grouped_swiglu call measured with rocprofv3 counters, if they were taken
-    on the current kernel source (else None)."""
+GEMM_SOURCE = os.path.join(ROOT, "grouped_gemm_weights_amd", "csrc", "grouped_swiglu.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_swiglu_traffic.json")
+# kernels of one moe_grouped_swiglu call
+GROUPED_KERNELS = ("plan_kernel", "gemm_stream_kernel", "gemm_wide_kernel")
+
+
+def _source_sha256():
     import hashlib
-    path = os.path.join(ROOT, "profiles", "grouped_swiglu_traffic.json")
-    if not os.path.exists(path):
+    return hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per moe_grouped_swiglu call of `workload` measured with rocprofv3 counters, if
+    they were taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
         return None
-    rec = json.load(open(path))
-    src = open(kernel_file, "rb").read()
-    if rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("kernel_source_sha256") != _source_sha256():
         return None
+    return rec.get("workloads", {}).get(workload)
+
+
+def write_traffic(prof_dir, workloads):
+    """Scale per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) by what the same counters read for the
+    calibration kernel (6 GiB read, 2 GiB written per launch) and record the per-call HBM bytes
+    of moe_grouped_swiglu for each workload."""
+    import collections
+    import csv
+
+    def load(sub):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(prof_dir, sub, "run_counter_collection.csv"))):
+            d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return d
+
+    def mean(v):
+        return sum(v) / len(v)
+
+    n = 1 << 30
+    cal_f = [v for k, v in load("cal_fetch").items() if "residual_kernel" in k][0]
+    cal_w = [v for k, v in load("cal_write").items() if "residual_kernel" in k][0]
+    fetch_scale = 6 * n / (mean(cal_f) * 1024)
+    write_scale = 2 * n / (mean(cal_w) * 1024)
+    rec = {
+        "kernel_source_sha256": _source_sha256(),
+        "calibration": {"kernel": "moe_residual_add over 2^30 elements (reads 6 GiB, writes 2 GiB)",
+                        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4)},
+        "workloads": {},
+    }
+    for cfg in workloads:
+        f, w = load(f"fetch_{cfg}"), load(f"write_{cfg}")
+        per = {}
+        for k in f:
+            if not any(s in k for s in GROUPED_KERNELS):
+                continue
+            short = k.replace("moe::(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+            per[short] = {"read_bytes": round(mean(f[k]) * 1024 * fetch_scale),
+                          "write_bytes": round(mean(w[k]) * 1024 * write_scale),
+                          "dispatches": len(f[k])}
+        rd = sum(v["read_bytes"] for v in per.values())
+        wr = sum(v["write_bytes"] for v in per.values())
+        rec["workloads"][cfg] = {
+            "per_kernel_per_launch": per, "read_bytes_per_call": rd, "write_bytes_per_call": wr,
+            "hbm_bytes_per_call": rd + wr,
+            "commands": [
+                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {prof_dir}/fetch_{cfg} -o run -- "
+                f"python3 bench.py --config {cfg} --steps 2 --warmup 1 --no-cpu-baseline",
+                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {prof_dir}/write_{cfg} -o run -- "
+                f"python3 bench.py --config {cfg} --steps 2 --warmup 1 --no-cpu-baseline",
+            ],
+        }
+    rec["calibration"]["commands"] = [
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {prof_dir}/cal_fetch -o run -- python3 bench.py --calibrate",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {prof_dir}/cal_write -o run -- python3 bench.py --calibrate",
+    ]
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
     return rec
 
 
 def main():
     args = parse()
+    if args.write_traffic:
+        rec = write_traffic(args.write_traffic, args.traffic_configs.split(","))
+        print(json.dumps(rec, indent=1))
+        return
     if args.calibrate:
         print(json.dumps(calibrate()), flush=True)
         return
@@ -330,8 +404,8 @@ def main():
                 "traffic": None}
     roof.update({"kernel": "moe_grouped_swiglu (tile plan + gate/up GEMM + down GEMM)",
                  "avg_ms": round(gemm_ms, 4), "alg_bytes": alg_bytes, "alg_flop": alg_flop})
-    tr = traffic_from_profiles(os.path.join(ROOT, "grouped_gemm_weights_amd", "csrc", "grouped_swiglu.hip"))
-    if tr is not None and tr.get("workload") == cfg.name:
+    tr = traffic_from_profiles(cfg.name)
+    if tr is not None:
         roof["traffic"] = tr["hbm_bytes_per_call"]
         roof["traffic_detail"] = {"read": tr["read_bytes_per_call"], "write": tr["write_bytes_per_call"],
                                   "source": "profiles/grouped_swiglu_traffic.json"}

@@ -5,7 +5,8 @@
 //  1. hist:    one block per chunk builds an LDS histogram of its expert ids.
 //  2. scan:    one block turns the chunk histograms into counts[e],
 //              offsets[e] (exclusive scan over e) and chunk_base[c][e] =
-//              offsets[e] + (rows of expert e in chunks before c).
+//              offsets[e] + (rows of expert e in chunks before c), several
+//              threads per expert so the chunk walk is not one long chain.
 //  3. scatter: one wave per chunk walks its assignments in order, 64 at a
 //              time; lanes holding the same expert find each other with one
 //              ballot per id bit, so an assignment's rank among equal ids of
@@ -61,39 +62,92 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = hist[e];
 }
 
-// One block of MOE_MAX_E threads; thread e owns expert e.
+// One block of MOE_MAX_E threads.  Expert e is owned by P = parts_per_expert(E)
+// threads (thread e * P + p), part p covering the chunk range
+// [p * cp, min((p + 1) * cp, n_chunks)), cp = ceil(n_chunks / P).  Pass 1 sums
+// each part's counts (loads batched so their latencies overlap), the parts are
+// prefixed per expert and the expert totals scanned in LDS, and pass 2 writes
+// chunk_base for each part from its starting value.
+constexpr int kScanBatch = 16;
+
+__host__ __device__ constexpr int parts_per_expert(int E) {
+  int p = 1;
+  while (p * 2 * E <= MOE_MAX_E && p < 64) p *= 2;
+  return p;
+}
+
 __global__ __launch_bounds__(MOE_MAX_E) void scan_kernel(const int32_t* __restrict__ chunk_counts,
                                                          int n_chunks, int E,
                                                          int32_t* __restrict__ chunk_base,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
-  __shared__ int32_t s[MOE_MAX_E];
-  const int e = threadIdx.x;
-  int32_t run = 0;
-  if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      const int64_t i = static_cast<int64_t>(c) * E + e;
-      const int32_t v = chunk_counts[i];
-      chunk_base[i] = run;
-      run += v;
+  __shared__ int32_t part[MOE_MAX_E];   // part sums, then the part's starting value
+  __shared__ int32_t s[MOE_MAX_E];      // expert totals, then their inclusive scan
+  const int P = parts_per_expert(E);
+  const int t = threadIdx.x;
+  const int e = t / P, p = t % P;
+  const bool owner = e < E;
+  const int cp = (n_chunks + P - 1) / P;
+  const int c0 = min(n_chunks, p * cp), c1 = min(n_chunks, c0 + cp);
+
+  int32_t sum = 0;
+  if (owner) {
+    for (int c = c0; c < c1; c += kScanBatch) {
+      int32_t v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        v[j] = 0;
+        if (c + j < c1) v[j] = chunk_counts[static_cast<int64_t>(c + j) * E + e];
+      }
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) sum += v[j];
     }
-    counts[e] = run;
   }
-  s[e] = e < E ? run : 0;
+  part[t] = sum;
+  __syncthreads();
+  // prefix of the parts of each expert (thread p == 0 of the expert), expert totals
+  int32_t total = 0;
+  if (owner && p == 0) {
+    for (int q = 0; q < P; ++q) {
+      const int32_t v = part[t + q];
+      part[t + q] = total;
+      total += v;
+    }
+  }
+  __syncthreads();
+  if (t < MOE_MAX_E) s[t] = 0;
+  __syncthreads();
+  if (owner && p == 0) {
+    s[e] = total;
+    counts[e] = total;
+  }
   __syncthreads();
   // inclusive Hillis-Steele scan over the experts
   for (int off = 1; off < MOE_MAX_E; off <<= 1) {
-    const int32_t add = e >= off ? s[e - off] : 0;
+    const int32_t add = t >= off ? s[t - off] : 0;
     __syncthreads();
-    s[e] += add;
+    s[t] += add;
     __syncthreads();
   }
-  const int32_t excl = s[e] - (e < E ? run : 0);
-  if (e < E) {
-    offsets[e] = excl;
-    for (int c = 0; c < n_chunks; ++c) chunk_base[static_cast<int64_t>(c) * E + e] += excl;
+  if (t == 0) offsets[E] = s[E - 1];
+  if (owner) {
+    const int32_t excl = e > 0 ? s[e - 1] : 0;
+    if (p == 0) offsets[e] = excl;
+    int32_t run = excl + part[t];
+    for (int c = c0; c < c1; c += kScanBatch) {
+      int32_t v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        v[j] = 0;
+        if (c + j < c1) v[j] = chunk_counts[static_cast<int64_t>(c + j) * E + e];
+      }
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (c + j < c1) chunk_base[static_cast<int64_t>(c + j) * E + e] = run;
+        run += v[j];
+      }
+    }
   }
-  if (e == E - 1) offsets[E] = s[e];
 }
 
 __global__ __launch_bounds__(kWave) void scatter_kernel(const int32_t* __restrict__ idx, int R,
