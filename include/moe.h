@@ -219,7 +219,7 @@ int moe_grouped_swiglu_workspace_size(int R, int E, int H, int I, moe_dtype dtyp
  *   status  device i32, may be NULL (MOE_STATUS_EXPERT_ABSENT when an expert
  *           with rows has slot -1; its rows are then left unwritten)
  * Errors: MOE_ERR_ARG for null pointers or sizes that disagree with w;
- * MOE_ERR_UNSUPPORTED when H or I is not a multiple of 8;
+ * MOE_ERR_UNSUPPORTED when H or I is not a multiple of 8 or H*I >= 2^31;
  * MOE_ERR_WORKSPACE when ws_bytes is too small.
  */
 int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int R, int E, int H, int I,
@@ -247,7 +247,9 @@ int moe_grouped_swiglu_range(const void* x_perm, const int32_t* offsets, int R, 
  * be called with x_perm = NULL and the [T*k][H] copy is never written.
  *   x      device [T][H] dtype; src_of device i32[T*k] (from moe_permute); k >= 1
  *   other arguments as moe_grouped_swiglu_range.
- * Errors: as moe_grouped_swiglu_range, plus MOE_ERR_ARG for k < 1 or a null src_of.
+ * Errors: as moe_grouped_swiglu_range, plus MOE_ERR_ARG for k < 1 or a null src_of,
+ * and MOE_ERR_UNSUPPORTED when R > 4*E (prefill tiles) and x spans 4 GiB or more
+ * ((R/k + 1) * H * 2 bytes): those tiles address x with 32-bit byte offsets.
  */
 int moe_grouped_swiglu_gathered(const void* x, const int32_t* src_of, int k, const int32_t* offsets,
                                 int R, int E, int H, int I, moe_dtype dtype, const moe_wbuf* w,
@@ -271,7 +273,7 @@ int moe_combine(const float* y_perm, const int32_t* row_of, const float* topk_w,
  * dense bf16 GEMM stands in for the attention block.
  *
  * moe_dense_gemm: out[M][N] = bf16(x[M][K] W[N][K]^T), bf16 in, f32 accumulate.
- *   K and N must be multiples of 8 (MOE_ERR_UNSUPPORTED otherwise).
+ *   K and N must be multiples of 8 and N*K below 2^31 (MOE_ERR_UNSUPPORTED otherwise).
  * moe_residual_add: out[i] = bf16(x[i] + y[i]) for i < n; x, out bf16, y f32;
  *   out may alias x.
  */
