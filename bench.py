@@ -41,9 +41,11 @@ def parse():
     p.add_argument("--config", default="r1_decode_t64")
     p.add_argument("--remote", choices=["routed", "all"], default="routed",
                    help="prefetch only the routed remote experts, or the whole remote share")
-    p.add_argument("--copy-mode", choices=["sdma", "any"], default="any",
+    p.add_argument("--copy-mode", choices=["sdma", "any", "kernel"], default="kernel",
                    help="any: hipMemcpyDefault (the runtime's copy path); sdma: the no-compute-unit "
-                        "copy kind")
+                        "copy kind; kernel: the library's copy kernel on --copy-blocks workgroups")
+    p.add_argument("--copy-blocks", type=int, default=0,
+                   help="workgroups of the copy kernel (--copy-mode kernel; 0: no limit)")
     p.add_argument("--alt-steps", type=int, default=5,
                    help="also time this many steps with the other copy mode (0: skip)")
     p.add_argument("--chunks", type=int, default=0,
@@ -157,6 +159,7 @@ def bench_pipeline(args, cfg, dev, copy_mode):
         "config": {"workload": cfg.name, "layers": n, "tokens": cfg.T, "hidden": cfg.H,
                    "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k,
                    "local_experts": cfg.n_local, "copy_engine": args.copy_mode,
+                   "copy_blocks": args.copy_blocks if args.copy_mode == "kernel" else None,
                    "merge": args.merge, "gather": args.gather, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -296,7 +299,8 @@ def main():
     cfg = synth.config(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    copy_mode = B.MOE_COPY_SDMA if args.copy_mode == "sdma" else B.MOE_COPY_ANY
+    copy_mode = {"sdma": B.MOE_COPY_SDMA, "any": B.MOE_COPY_ANY,
+                 "kernel": B.copy_kernel_on(args.copy_blocks)}[args.copy_mode]
     if cfg.layers != 1:
         print(json.dumps(bench_pipeline(args, cfg, dev, copy_mode)), flush=True)
         return
@@ -358,7 +362,8 @@ def main():
     alt = None
     if args.alt_steps > 0:
         # the same step with the other copy path, for comparison (not the reported value)
-        L.copy_mode = B.MOE_COPY_ANY if copy_mode == B.MOE_COPY_SDMA else B.MOE_COPY_SDMA
+        alt_name = "sdma" if args.copy_mode == "any" else "any"
+        L.copy_mode = B.MOE_COPY_SDMA if alt_name == "sdma" else B.MOE_COPY_ANY
         for i in range(2):
             step(i, False)
         torch.cuda.synchronize()
@@ -367,7 +372,7 @@ def main():
             step(i, False)
         torch.cuda.synchronize()
         alt_s = (time.perf_counter() - ta) / args.alt_steps
-        alt = {"copy_engine": "sdma" if copy_mode == B.MOE_COPY_ANY else "any",
+        alt = {"copy_engine": alt_name,
                "ms_per_step": round(alt_s * 1e3, 3), "tokens_per_s": round(cfg.T / alt_s, 1)}
         L.copy_mode = copy_mode
 
@@ -426,6 +431,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I,
                    "experts": cfg.E, "top_k": cfg.k, "local_experts": cfg.n_local,
                    "remote_fetch": args.remote, "copy_engine": args.copy_mode,
+                   "copy_blocks": args.copy_blocks if args.copy_mode == "kernel" else None,
                    "merge": args.merge, "gather": args.gather, "fetch_chunks": nch, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "breakdown_ms": {"route_permute": round(rp_ms, 4), "merge_prefetch_copy": round(copy_ms, 4),

@@ -18,7 +18,14 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 MOE_F32, MOE_BF16 = 0, 1
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_STATUS_NONFINITE_LOGIT, MOE_STATUS_EXPERT_ABSENT, MOE_STATUS_BAD_EXPERT_ID = 1, 2, 4
-MOE_COPY_SDMA, MOE_COPY_ANY = 0, 1
+MOE_COPY_SDMA, MOE_COPY_ANY, MOE_COPY_KERNEL = 0, 1, 2
+
+
+def copy_kernel_on(n_blocks: int) -> int:
+    """MOE_COPY_KERNEL_ON(n): the library's copy kernel on at most n workgroups (0: no limit)."""
+    if not 0 <= n_blocks <= 0xFFFF:
+        raise ValueError(f"copy kernel workgroups {n_blocks} outside [0, 65535]")
+    return MOE_COPY_KERNEL | (n_blocks << 8)
 
 # Every symbol include/moe.h declares (checked by the CPU tests).
 EXPORTS = (

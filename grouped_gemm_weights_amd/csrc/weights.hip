@@ -13,7 +13,11 @@
 // MOE_COPY_SDMA a device-to-device copy is issued as
 // hipMemcpyDeviceToDeviceNoCU, which the runtime executes on an SDMA engine
 // and never on the compute units (DWDP explainer, "stay data-parallel" panel:
-// the pull runs on the copy engine, off the compute units).
+// the pull runs on the copy engine, off the compute units).  With
+// MOE_COPY_KERNEL_ON(n) it is the library's streaming copy kernel on at most n
+// workgroups: on one GPU, where the stand-in pull is an HBM-to-HBM copy, this
+// keeps it on a bounded set of compute units instead of spreading a runtime
+// copy kernel over the whole chip under a concurrent grouped GEMM.
 #include <vector>
 
 #include "common.h"
@@ -69,23 +73,79 @@ int check_pool(const char* who, const moe_pool* p, const moe_wbuf* dst) {
   return MOE_OK;
 }
 
-int copy_kind(const char* who, const void* src, int copy_mode, hipMemcpyKind* kind) {
-  if (copy_mode != MOE_COPY_SDMA && copy_mode != MOE_COPY_ANY)
+// How a pool's runs are copied: a runtime copy of `kind`, or (kernel_blocks >= 0) the
+// library's copy kernel on at most kernel_blocks workgroups (0: no limit).
+struct CopyPlan {
+  hipMemcpyKind kind;
+  int kernel_blocks;
+};
+
+constexpr int kCopyThreads = 1024;
+constexpr int kCopyUnroll = 8;
+constexpr int kCopyMaxBlocks = 2048;
+
+int copy_plan(const char* who, const void* src, int copy_mode, CopyPlan* plan) {
+  const int base = copy_mode & 0xff, blocks = copy_mode >> 8;
+  if (copy_mode < 0 || (base != MOE_COPY_SDMA && base != MOE_COPY_ANY && base != MOE_COPY_KERNEL) ||
+      (base != MOE_COPY_KERNEL && blocks != 0))
     return fail(MOE_ERR_ARG, "%s: bad copy_mode %d", who, copy_mode);
-  if (copy_mode == MOE_COPY_ANY) {
-    *kind = hipMemcpyDefault;
-    return MOE_OK;
-  }
+  plan->kernel_blocks = -1;
+  plan->kind = hipMemcpyDefault;
+  if (base == MOE_COPY_ANY) return MOE_OK;
   hipPointerAttribute_t attr;
   hipError_t e = hipPointerGetAttributes(&attr, src);
   if (e != hipSuccess) return hip_fail(e, "hipPointerGetAttributes(pool)");
-  *kind = (attr.type == hipMemoryTypeHost) ? hipMemcpyHostToDevice : hipMemcpyDeviceToDeviceNoCU;
+  const bool host = attr.type == hipMemoryTypeHost;
+  if (base == MOE_COPY_SDMA) {
+    plan->kind = host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDeviceNoCU;
+  } else if (host) {
+    plan->kind = hipMemcpyHostToDevice;
+  } else {
+    plan->kernel_blocks = blocks;
+  }
   return MOE_OK;
 }
 
-// Copy the experts of ids that the pool holds into their slots; returns bytes issued.
+// dst[i] = src[i] for i < n16 (16-byte units); each thread keeps kCopyUnroll loads in flight
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(const uint4* __restrict__ src,
+                                                            uint4* __restrict__ dst, int64_t n16) {
+  const int64_t step = static_cast<int64_t>(gridDim.x) * kCopyThreads * kCopyUnroll;
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * kCopyThreads * kCopyUnroll + threadIdx.x;
+       i0 < n16; i0 += step) {
+    uint4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * kCopyThreads;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (i < n16) v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * kCopyThreads;
+      if (i < n16) dst[i] = v[u];
+    }
+  }
+}
+
+int copy_run(void* to, const void* from, size_t bytes, const CopyPlan& plan, hipStream_t s) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(to) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(from) % 16 == 0) && (bytes % 16 == 0);
+  if (plan.kernel_blocks < 0 || !aligned) {
+    MOE_HIP_CHECK(hipMemcpyAsync(to, from, bytes, plan.kernel_blocks < 0 ? plan.kind : hipMemcpyDefault, s));
+    return MOE_OK;
+  }
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  int64_t blocks = ceil_div64(n16, static_cast<int64_t>(kCopyThreads) * kCopyUnroll);
+  blocks = std::min<int64_t>(blocks, plan.kernel_blocks > 0 ? plan.kernel_blocks : kCopyMaxBlocks);
+  hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCopyThreads), 0, s,
+                     static_cast<const uint4*>(from), static_cast<uint4*>(to), n16);
+  MOE_LAUNCH_CHECK("copy kernel launch");
+  return MOE_OK;
+}
+
+// Copy the experts of ids that the pool holds into their slots.
 int copy_pool_experts(const moe_pool* p, const int32_t* ids, int n, moe_wbuf* dst,
-                      hipStream_t s, hipMemcpyKind kind) {
+                      hipStream_t s, const CopyPlan& plan) {
   const int64_t eb = dst->expert_bytes;
   const int64_t lo = p->first_expert, hi = lo + p->n_experts;
   auto in_pool = [&](int32_t e) { return e >= lo && e < hi; };
@@ -100,7 +160,10 @@ int copy_pool_experts(const moe_pool* p, const int32_t* ids, int n, moe_wbuf* ds
     const char* src = static_cast<const char*>(p->base) + (ids[i] - lo) * eb;
     char* to = static_cast<char*>(dst->base) + static_cast<int64_t>(i) * eb;
     // a run already in place (the local block stitched at the head of the range) needs no copy
-    if (src != to) MOE_HIP_CHECK(hipMemcpyAsync(to, src, static_cast<size_t>(j - i) * eb, kind, s));
+    if (src != to) {
+      const int rc = copy_run(to, src, static_cast<size_t>(j - i) * eb, plan, s);
+      if (rc) return rc;
+    }
     i = j;
   }
   return MOE_OK;
@@ -118,8 +181,8 @@ extern "C" int moe_merge_weights(const moe_pool* local, const int32_t* ids_host,
   if (!dst->slot_of) return fail(MOE_ERR_ARG, "moe_merge_weights: null slot map");
   rc = check_pool("moe_merge_weights", local, dst);
   if (rc) return rc;
-  hipMemcpyKind kind;
-  rc = copy_kind("moe_merge_weights", local->base, copy_mode, &kind);
+  CopyPlan plan;
+  rc = copy_plan("moe_merge_weights", local->base, copy_mode, &plan);
   if (rc) return rc;
   hipStream_t s = as_stream(stream);
   if (wait_free) MOE_HIP_CHECK(hipStreamWaitEvent(s, as_event(wait_free), 0));
@@ -134,7 +197,7 @@ extern "C" int moe_merge_weights(const moe_pool* local, const int32_t* ids_host,
     hipLaunchKernelGGL(slot_set_kernel, dim3(1), dim3(kSlotIdsPerLaunch), 0, s, dst->slot_of, c);
     MOE_LAUNCH_CHECK("moe_merge_weights: slot set");
   }
-  rc = copy_pool_experts(local, ids_host, n_ids, dst, s, kind);
+  rc = copy_pool_experts(local, ids_host, n_ids, dst, s, plan);
   if (rc) return rc;
   if (ready) MOE_HIP_CHECK(hipEventRecord(as_event(ready), s));
   return MOE_OK;
@@ -148,12 +211,12 @@ extern "C" int moe_prefetch_layer(const moe_pool* remote, const int32_t* ids_hos
   if (rc) return rc;
   rc = check_pool("moe_prefetch_layer", remote, dst);
   if (rc) return rc;
-  hipMemcpyKind kind;
-  rc = copy_kind("moe_prefetch_layer", remote->base, copy_mode, &kind);
+  CopyPlan plan;
+  rc = copy_plan("moe_prefetch_layer", remote->base, copy_mode, &plan);
   if (rc) return rc;
   hipStream_t s = as_stream(copy_stream);
   if (wait_free) MOE_HIP_CHECK(hipStreamWaitEvent(s, as_event(wait_free), 0));
-  rc = copy_pool_experts(remote, ids_host, n_ids, dst, s, kind);
+  rc = copy_pool_experts(remote, ids_host, n_ids, dst, s, plan);
   if (rc) return rc;
   if (ready) MOE_HIP_CHECK(hipEventRecord(as_event(ready), s));
   return MOE_OK;

@@ -162,9 +162,9 @@ class MoEPipeline:
         L, cs, ps = self.L, self.L.compute_stream, self.L.copy_stream
         self.reset()
         for l in range(self.n):
+            cs.synchronize()               # the previous layer's compute is done
             self.fill(l, wait_free=True, ev=ev)
             ps.synchronize()
-            cs.synchronize()
             if ev is not None:
                 B.moe_event_record(ev["d0"][l], cs)
             self.dense(l)

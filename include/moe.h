@@ -75,6 +75,12 @@ enum {
 /* copy-engine selection for moe_merge_weights / moe_prefetch_layer */
 #define MOE_COPY_SDMA 0 /* device-to-device copies on the SDMA engines, no compute units */
 #define MOE_COPY_ANY 1  /* let the runtime choose (it may use a copy kernel on the CUs) */
+/* The library's own streaming copy kernel for device-to-device runs, on at most n
+ * workgroups of 1024 threads (n = 0: as many as the copy can use).  A small n keeps the
+ * pull on a bounded set of compute units, so a grouped GEMM running beside it (one
+ * workgroup per CU) keeps the rest; host-memory sources still use the runtime copy. */
+#define MOE_COPY_KERNEL 2
+#define MOE_COPY_KERNEL_ON(n) (MOE_COPY_KERNEL | ((n) << 8))
 
 /* Limits of the kernels (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_E 1024
@@ -173,7 +179,7 @@ int moe_permute(const int32_t* topk_idx, int T, int E, int k, const void* x, int
  *   wait_free if not NULL, the stream first waits for it (the last reader of
  *             this half is done)
  *   ready     if not NULL, recorded on the stream after the copies
- *   copy_mode MOE_COPY_SDMA or MOE_COPY_ANY
+ *   copy_mode MOE_COPY_SDMA, MOE_COPY_ANY or MOE_COPY_KERNEL_ON(n), n in [0, 65535]
  * Copies of consecutive ids in consecutive slots are coalesced, and a run
  * whose source bytes are its destination bytes is skipped: when the merged
  * range is stitched with the local-expert block at its head (moe_vmm_map

@@ -59,6 +59,18 @@ def test_host_side_argument_errors(B):
     with pytest.raises(B.MoEError) as e:
         B.moe_prefetch_layer(B.pool(1 << 22, 64, 4, 4), [4], buf)   # block size mismatch
     assert e.value.code == B.MOE_ERR_ARG
+    # copy modes: unknown kind, a workgroup count on a runtime copy kind, negative
+    for mode in (3, B.MOE_COPY_ANY | (4 << 8), B.MOE_COPY_SDMA | (1 << 8), -1):
+        with pytest.raises(B.MoEError) as e:
+            B.moe_prefetch_layer(B.pool(1 << 22, 96, 4, 4), [4], buf, copy_mode=mode)
+        assert e.value.code == B.MOE_ERR_ARG
+    assert B.copy_kernel_on(32) == (2 | 32 << 8)
+    with pytest.raises(ValueError):
+        B.copy_kernel_on(1 << 16)
+    with pytest.raises(B.MoEError) as e:
+        B.moe_grouped_swiglu(1, 1, 8, 8, 1 << 16, 1 << 15, B.MOE_BF16,
+                             B.wbuf(1, 3 * (1 << 31) * 2, 8, 8, 1), 1, 1 << 40, 1)
+    assert e.value.code == B.MOE_ERR_UNSUPPORTED                  # H*I = 2^31
     with pytest.raises(B.MoEError) as e:
         B.moe_grouped_swiglu(1, 1, 8, 8, 12, 8, B.MOE_BF16, B.wbuf(1, 3 * 12 * 8 * 2, 8, 8, 1), 1, 1 << 30, 1)
     assert e.value.code == B.MOE_ERR_UNSUPPORTED                  # H not a multiple of 8

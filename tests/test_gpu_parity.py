@@ -106,14 +106,16 @@ def test_merged_buffer_bytes_and_slot_map():
     merged = O.merge(pools, ids)
     got = base.cpu().numpy()[: len(ids)].view(np.int16)
     assert got.tobytes() == merged.tobytes()
-    # copy engine chosen by the runtime gives the same bytes
-    base.fill_(0)
-    torch.cuda.synchronize()
+    # the runtime's copy and the library's copy kernel (one workgroup, and unbounded)
+    # give the same bytes
     from grouped_gemm_weights_amd import binding as B
-    B.moe_merge_weights(L.local_pool, ids, L.wbufs[1], L.copy_stream, copy_mode=B.MOE_COPY_ANY)
-    B.moe_prefetch_layer(L.remote_pool, ids, L.wbufs[1], L.copy_stream, copy_mode=B.MOE_COPY_ANY)
-    L.synchronize()
-    assert base.cpu().numpy()[: len(ids)].view(np.int16).tobytes() == merged.tobytes()
+    for mode in (B.MOE_COPY_ANY, B.copy_kernel_on(1), B.copy_kernel_on(0)):
+        base.fill_(0)
+        torch.cuda.synchronize()
+        B.moe_merge_weights(L.local_pool, ids, L.wbufs[1], L.copy_stream, copy_mode=mode)
+        B.moe_prefetch_layer(L.remote_pool, ids, L.wbufs[1], L.copy_stream, copy_mode=mode)
+        L.synchronize()
+        assert base.cpu().numpy()[: len(ids)].view(np.int16).tobytes() == merged.tobytes(), mode
 
 
 # ----------------------------------------------------------------------------
