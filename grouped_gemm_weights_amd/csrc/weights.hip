@@ -82,7 +82,9 @@ struct CopyPlan {
 
 constexpr int kCopyThreads = 1024;
 constexpr int kCopyUnroll = 8;
-constexpr int kCopyMaxBlocks = 2048;
+constexpr int64_t kCopyMaxBlocks = int64_t{1} << 20;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 int copy_plan(const char* who, const void* src, int copy_mode, CopyPlan* plan) {
   const int base = copy_mode & 0xff, blocks = copy_mode >> 8;
@@ -106,23 +108,25 @@ int copy_plan(const char* who, const void* src, int copy_mode, CopyPlan* plan) {
   return MOE_OK;
 }
 
-// dst[i] = src[i] for i < n16 (16-byte units); each thread keeps kCopyUnroll loads in flight
-__global__ __launch_bounds__(kCopyThreads) void copy_kernel(const uint4* __restrict__ src,
-                                                            uint4* __restrict__ dst, int64_t n16) {
+// dst[i] = src[i] for i < n16 (16-byte units); each thread keeps kCopyUnroll loads in flight.
+// Loads and stores are non-temporal: the pulled weights are read once, and streaming them
+// through L2 would evict what a grouped GEMM running beside the pull is reusing.
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(const u32x4* __restrict__ src,
+                                                            u32x4* __restrict__ dst, int64_t n16) {
   const int64_t step = static_cast<int64_t>(gridDim.x) * kCopyThreads * kCopyUnroll;
   for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * kCopyThreads * kCopyUnroll + threadIdx.x;
        i0 < n16; i0 += step) {
-    uint4 v[kCopyUnroll];
+    u32x4 v[kCopyUnroll];
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
       const int64_t i = i0 + static_cast<int64_t>(u) * kCopyThreads;
-      v[u] = make_uint4(0, 0, 0, 0);
-      if (i < n16) v[u] = src[i];
+      v[u] = u32x4{0, 0, 0, 0};
+      if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
       const int64_t i = i0 + static_cast<int64_t>(u) * kCopyThreads;
-      if (i < n16) dst[i] = v[u];
+      if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
     }
   }
 }
@@ -138,7 +142,7 @@ int copy_run(void* to, const void* from, size_t bytes, const CopyPlan& plan, hip
   int64_t blocks = ceil_div64(n16, static_cast<int64_t>(kCopyThreads) * kCopyUnroll);
   blocks = std::min<int64_t>(blocks, plan.kernel_blocks > 0 ? plan.kernel_blocks : kCopyMaxBlocks);
   hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCopyThreads), 0, s,
-                     static_cast<const uint4*>(from), static_cast<uint4*>(to), n16);
+                     static_cast<const u32x4*>(from), static_cast<u32x4*>(to), n16);
   MOE_LAUNCH_CHECK("copy kernel launch");
   return MOE_OK;
 }
