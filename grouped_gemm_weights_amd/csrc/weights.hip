@@ -65,7 +65,8 @@ int check_ids(const char* who, const int32_t* ids, int n, const moe_wbuf* dst) {
 }
 
 int check_pool(const char* who, const moe_pool* p, const moe_wbuf* dst) {
-  if (!p || !p->base || p->n_experts < 0 || p->first_expert < 0)
+  // an empty pool (n_experts == 0) may have a null base
+  if (!p || (!p->base && p->n_experts != 0) || p->n_experts < 0 || p->first_expert < 0)
     return fail(MOE_ERR_ARG, "%s: bad pool", who);
   if (p->expert_bytes != dst->expert_bytes)
     return fail(MOE_ERR_ARG, "%s: pool expert_bytes %lld != buffer %lld", who,
@@ -93,7 +94,7 @@ int copy_plan(const char* who, const void* src, int copy_mode, CopyPlan* plan) {
     return fail(MOE_ERR_ARG, "%s: bad copy_mode %d", who, copy_mode);
   plan->kernel_blocks = -1;
   plan->kind = hipMemcpyDefault;
-  if (base == MOE_COPY_ANY) return MOE_OK;
+  if (base == MOE_COPY_ANY || !src) return MOE_OK;   // !src: an empty pool, nothing to copy
   hipPointerAttribute_t attr;
   hipError_t e = hipPointerGetAttributes(&attr, src);
   if (e != hipSuccess) return hip_fail(e, "hipPointerGetAttributes(pool)");

@@ -91,13 +91,19 @@ class MoELayer:
             dev_index = d.index if d.index is not None else torch.cuda.current_device()
             local_bytes = cfg.n_local * self.eb
             own_bytes = (self.n_slots - cfg.n_local) * self.eb
-            self._local_phys = B.moe_vmm_create(local_bytes, dev_index)
-            self._vmm_phys.append(self._local_phys)
+            if local_bytes == 0 and own_bytes == 0:
+                raise ValueError("stitched halves need at least one slot")
+            self._local_phys = B.moe_vmm_create(local_bytes, dev_index) if local_bytes else None
+            if self._local_phys is not None:
+                self._vmm_phys.append(self._local_phys)
             for h in range(n_halves):
-                own = B.moe_vmm_create(own_bytes, dev_index)
-                self._vmm_phys.append(own)
-                va = B.moe_vmm_map([self._local_phys, own], [local_bytes, own_bytes], dev_index)
-                self._vmm_ranges.append((va, [local_bytes, own_bytes]))
+                own = B.moe_vmm_create(own_bytes, dev_index) if own_bytes else None
+                if own is not None:
+                    self._vmm_phys.append(own)
+                # a block of zero bytes (no local experts, or no slots beyond them) is left out
+                pieces = [(ph, nb) for ph, nb in ((self._local_phys, local_bytes), (own, own_bytes)) if nb]
+                va = B.moe_vmm_map([ph for ph, _ in pieces], [nb for _, nb in pieces], dev_index)
+                self._vmm_ranges.append((va, [nb for _, nb in pieces]))
                 self.halves.append((va, self.slot_maps[h]))
                 self.wbufs.append(B.wbuf(va, self.eb, self.n_slots, E, self.slot_maps[h]))
                 self.stitched_local_pools.append(B.pool(va, self.eb, 0, cfg.n_local))

@@ -92,6 +92,7 @@ enum {
  * or in pinned host memory.  The local pool is this rank's resident share;
  * the remote pool stands in for the peers' shares (DWDP abstract: MoE weights
  * are offloaded across peer GPUs and missing experts fetched on demand).
+ * An empty pool (n_experts == 0: every expert local, or none) may have base NULL.
  */
 typedef struct moe_pool {
   const void* base;

@@ -67,6 +67,43 @@ def test_small_bf16_layers(T, H, I, E, k, n_local, zipf):
         np.testing.assert_array_equal(out["y"], out["y_perm"][out["row_of"]])
 
 
+@pytest.mark.parametrize("T,H,I,E,k,n_local,stitched", [
+    (20, 64, 32, 4, 4, 2, False),          # k = E: every token picks every expert
+    (30, 64, 32, 1, 1, 1, False),          # a single expert, all local
+    (16, 64, 32, 1024, 8, 256, False),     # E at the kernel limit (MOE_MAX_E)
+    (8, 64, 32, 64, 64, 16, False),        # k at the kernel limit (MOE_MAX_K)
+    (40, 64, 32, 16, 2, 0, False),         # every expert remote (empty local pool)
+    (40, 64, 32, 16, 2, 16, False),        # every expert local (empty remote pool)
+    (24, 1024, 1024, 8, 2, 0, True),       # stitched half with no local block
+    (24, 1024, 1024, 8, 2, 8, True),       # stitched half with no fetched block
+], ids=["k_eq_E", "one_expert", "E_max", "k_max", "all_remote", "all_local",
+        "stitched_all_remote", "stitched_all_local"])
+def test_edge_layers(T, H, I, E, k, n_local, stitched):
+    cfg = synth.MoEConfig(f"bf16_edge_T{T}_E{E}_k{k}_l{n_local}", T=T, H=H, I=I, E=E, k=k,
+                          dtype="bf16", n_local=n_local, seed=77 + T + E)
+    log(f"case {cfg.name} stitched={stitched}")
+    L = build_layer(cfg, stitched=stitched)
+    try:
+        _run(L)
+        out, ref = check_full(cfg, L)
+        assert out["counts"].sum() == T * k
+        if k == E:
+            np.testing.assert_array_equal(out["counts"], np.full(E, T))
+    finally:
+        L.close()
+
+
+def test_empty_batch():
+    cfg = synth.MoEConfig("bf16_empty", T=0, H=64, I=32, E=8, k=2, dtype="bf16", n_local=4, seed=5)
+    log(f"case {cfg.name}")
+    L = _run(build_layer(cfg))
+    out = L.outputs()
+    assert out["status"] == 0
+    np.testing.assert_array_equal(out["counts"], np.zeros(cfg.E, np.int32))
+    np.testing.assert_array_equal(out["offsets"], np.zeros(cfg.E + 1, np.int32))
+    assert out["y"].shape == (0, cfg.H) and out["y_perm"].shape == (0, cfg.H)
+
+
 def test_all_tokens_one_expert_and_prefill_tiles():
     cfg = synth.MoEConfig("bf16_one_hot", T=700, H=128, I=96, E=12, k=2, dtype="bf16", n_local=3,
                           seed=5)
