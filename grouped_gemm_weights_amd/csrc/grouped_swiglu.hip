@@ -1,22 +1,24 @@
 // moe_grouped_swiglu: the grouped GEMM over the experts of the merged buffer,
 // with each expert's SwiGLU FFN, and moe_dense_gemm (the pipeline's dense
-// stand-in block), which runs the same tile loop on one weight matrix.
+// stand-in block), which runs the prefill tile loop on one weight matrix.
 //
-// bf16 path (gfx950 MFMA, v_mfma_f32_16x16x32_bf16, fp32 accumulate):
+// bf16 path (gfx950 MFMA, fp32 accumulate):
 //   1. plan:  one block turns offsets[] into a list of BM-row tiles
 //             (expert, first row, rows, slot), expert-major, and checks that
 //             every expert with rows has a slot in the merged buffer.
-//   2. gemm1: per (tile, 64-column block): g = X Wg^T and u = X Wu^T share the
-//             A tile; the epilogue writes h = bf16(silu(g) * u).
+//   2. gemm1: per (tile, column block): g = X Wg^T and u = X Wu^T share the
+//             A rows; the epilogue writes h = bf16(silu(g) * u).
 //   3. gemm2: per (tile, column block): y_perm = h Wd^T in fp32.
-// Both GEMMs stage A and B tiles through LDS, double-buffered, with the next
-// K step's global loads in flight while the current one feeds the MFMAs.
 // Weights are stored output-major ([N][K], K contiguous), so every operand
 // row is a contiguous 16-byte vector per lane, as the MFMA wants it.
 //
-// Two tile shapes are compiled: a decode shape (16-row tiles; the expert
-// groups hold a few rows and the kernel streams weights) and a prefill shape
-// (128-row tiles, MFMA-bound).  The host picks by the average rows per expert.
+// Two tile kernels, picked by the average rows per expert:
+//   decode  (<= 4 rows per expert on average): 16-row tiles, gemm_stream_kernel
+//           streams each weight row once from HBM straight into 16x16x32 MFMA
+//           operand registers (no LDS): the call is bound by weight bytes.
+//   prefill: 256-row tiles, gemm_wide_kernel: one wave per SIMD with 128 x 128
+//           accumulator quarters, 32x32x16 MFMA, LDS double buffer, a hand-
+//           pipelined K loop; MFMA-bound.
 //
 // f32 path (tiny exact-check workloads): plain fp32 FMA kernels, one thread
 // per output element, fp32 throughout.
