@@ -37,7 +37,8 @@ struct Tile {
   int32_t slot;
 };
 
-constexpr int kMinBM = 16;  // smallest tile height: bounds the tile list
+constexpr int kMinBM = 16;        // smallest tile height: bounds the tile list
+constexpr int kWidePlanBM = 256;  // prefill tile height: tiles split into heavy and light lists
 
 int64_t max_tiles(int64_t R, int E) { return ceil_div64(R, kMinBM) + std::min<int64_t>(E, R); }
 
@@ -58,42 +59,62 @@ SwigluWs swiglu_ws(int64_t R, int E, int I, moe_dtype dt) {
 // tile plan
 // ---------------------------------------------------------------------------
 
+// Tiles of BM rows per expert.  Decode tiles (BM < 256) go out expert-major.
+// Prefill tiles are split into two expert-major lists: heavy tiles (more than
+// 3/4 of BM rows, MFMA-bound) at [0, n_heavy) and light tiles (an expert's
+// short last tile, bound by streaming that expert's weights) at
+// [n_heavy, n_heavy + n_light), so the GEMM can interleave the two kinds.
+// n_tiles[0] = all tiles, n_tiles[1] = heavy, n_tiles[2] = light.
 __global__ __launch_bounds__(MOE_MAX_E) void plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                          int e_begin, int e_end,
                                                          int BM, const int32_t* __restrict__ slot_of,
                                                          Tile* __restrict__ tiles,
                                                          int32_t* __restrict__ n_tiles,
                                                          int32_t* status) {
-  __shared__ int32_t s[MOE_MAX_E];
+  __shared__ int64_t s[MOE_MAX_E];   // heavy count in the low 32 bits, light count in the high
   const int e = threadIdx.x;
-  int nt = 0, lo = 0, cnt = 0, slot = -1;
+  int nh = 0, nl = 0, lo = 0, cnt = 0, slot = -1;
   if (e < E && e >= e_begin && e < e_end) {
     lo = offsets[e];
     cnt = offsets[e + 1] - lo;
     if (cnt > 0) {
       slot = slot_of[e];
-      if (slot < 0) status_or(status, MOE_STATUS_EXPERT_ABSENT);
-      else nt = (cnt + BM - 1) / BM;
+      if (slot < 0) {
+        status_or(status, MOE_STATUS_EXPERT_ABSENT);
+      } else if (BM < kWidePlanBM) {
+        nh = (cnt + BM - 1) / BM;
+      } else {
+        const int rem = cnt % BM;
+        nh = cnt / BM + (4 * rem > 3 * BM ? 1 : 0);
+        nl = (rem > 0 && 4 * rem <= 3 * BM) ? 1 : 0;
+      }
     }
   }
-  s[e] = nt;
+  s[e] = static_cast<int64_t>(nh) | (static_cast<int64_t>(nl) << 32);
   __syncthreads();
   for (int off = 1; off < MOE_MAX_E; off <<= 1) {
-    const int32_t add = e >= off ? s[e - off] : 0;
+    const int64_t add = e >= off ? s[e - off] : 0;
     __syncthreads();
     s[e] += add;
     __syncthreads();
   }
-  const int start = s[e] - nt;
-  for (int i = 0; i < nt; ++i) {
+  const int n_heavy = static_cast<int>(s[MOE_MAX_E - 1] & 0xffffffff);
+  const int n_light = static_cast<int>(s[MOE_MAX_E - 1] >> 32);
+  const int h0 = static_cast<int>(s[e] & 0xffffffff) - nh;
+  const int l0 = static_cast<int>(s[e] >> 32) - nl;
+  for (int i = 0; i < nh + nl; ++i) {
     Tile t;
     t.expert = e;
     t.row0 = lo + i * BM;
     t.rows = min(BM, cnt - i * BM);
     t.slot = slot;
-    tiles[start + i] = t;
+    tiles[i < nh ? h0 + i : n_heavy + l0] = t;
   }
-  if (e == MOE_MAX_E - 1) *n_tiles = s[e];
+  if (e == 0) {
+    n_tiles[0] = n_heavy + n_light;
+    n_tiles[1] = n_heavy;
+    n_tiles[2] = n_light;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -106,9 +127,12 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)
 // Prefill work order: groups of kMGroup consecutive m-tiles sweep all n-tiles
 // together on one XCD (workgroup i runs on XCD i % 8), so the blocks that run
 // at the same time there share A tiles and weight panels in its L2; groups go
-// round-robin over the XCDs, which spreads hot and light experts evenly (a
-// split into 8 contiguous ranges left one XCD 17 % over the mean under Zipf
-// routing).
+// round-robin over the XCDs (a split into 8 contiguous ranges left one XCD 17 %
+// over the mean under Zipf routing).  Heavy groups (full tiles, MFMA-bound) are
+// spread evenly among light ones (an expert's short last tile, bound by
+// streaming the expert's weights from HBM), so at any time some CUs stream
+// weights while others compute, instead of a hot expert's tiles running
+// together and leaving HBM idle.
 // ---------------------------------------------------------------------------
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -390,18 +414,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int BM = kWideBM;
   constexpr int OUTN = DUAL ? kWideBN / 2 : kWideBN;
 
-  const int n_m = tiles ? *n_tiles : (dense_M + BM - 1) / BM;
+  // heavy (MFMA-bound) and light (weight-streaming) tiles, each list cut into groups of
+  // kMGroup; group position gp holds a heavy group when the count of heavy groups up to
+  // it, floor((gp + 1) F / G), steps up, so the F heavy groups spread evenly over all G
+  const int n_heavy = tiles ? n_tiles[1] : (dense_M + BM - 1) / BM;
+  const int n_light = tiles ? n_tiles[2] : 0;
   const int n_n = (N + OUTN - 1) / OUTN;
-  const int total = n_m * n_n;
+  const int F = (n_heavy + kMGroup - 1) / kMGroup, P = (n_light + kMGroup - 1) / kMGroup;
+  const int G = F + P;
   const int per_group = n_n * kMGroup;
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
-  const int g = (local / per_group) * kXcds + xcd;
-  if (g * kMGroup >= n_m) return;
-  const int gsize = min(kMGroup, n_m - g * kMGroup);
+  const int gp = (local / per_group) * kXcds + xcd;
+  if (gp >= G) return;
+  const int64_t c0 = static_cast<int64_t>(gp) * F / G, c1 = static_cast<int64_t>(gp + 1) * F / G;
+  const bool heavy = c1 > c0;
+  const int gi = heavy ? static_cast<int>(c0) : gp - static_cast<int>(c1);
+  const int first = heavy ? gi * kMGroup : n_heavy + gi * kMGroup;
+  const int gsize = min(kMGroup, (heavy ? n_heavy : n_light) - gi * kMGroup);
   const int rem = local % per_group;
   if (rem >= gsize * n_n) return;
   const int nt = rem / gsize;
-  const int mt = g * kMGroup + rem % gsize;
+  const int mt = first + rem % gsize;
 
   Tile tile;
   if (tiles) {
@@ -452,7 +485,8 @@ struct GemmWide {
     }
     if (grid_m <= 0) return MOE_OK;
     const int outn = DUAL ? 128 : 256;
-    const int64_t groups = ceil_div64(grid_m, kMGroup);
+    // heavy and light groups: at most one more group than one list of grid_m tiles
+    const int64_t groups = ceil_div64(grid_m, kMGroup) + 1;
     const int64_t blocks = ceil_div64(groups, kXcds) * kXcds * kMGroup * ceil_div(N, outn);
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), kLds, s, A, lda, a_index,
                        a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles, dense_M,
