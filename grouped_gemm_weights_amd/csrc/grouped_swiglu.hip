@@ -475,14 +475,11 @@ struct GemmWide {
                     hipStream_t s) {
     auto kern = K % 64 == 0 ? gemm_wide_kernel<DUAL, OUT_BF16, true>
                             : gemm_wide_kernel<DUAL, OUT_BF16, false>;
-    static bool configured = false;
-    if (!configured) {
-      for (auto k : {gemm_wide_kernel<DUAL, OUT_BF16, true>, gemm_wide_kernel<DUAL, OUT_BF16, false>})
-        MOE_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                          static_cast<int>(kLds)));
-      configured = true;
-    }
+    // the dynamic-LDS limit above 64 KB is set on every launch: it is a cheap host call
+    // and, unlike a once-per-process flag, holds for every device and thread
+    MOE_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      static_cast<int>(kLds)));
     if (grid_m <= 0) return MOE_OK;
     const int outn = DUAL ? 128 : 256;
     // heavy and light groups: at most one more group than one list of grid_m tiles
