@@ -44,7 +44,7 @@ class MoELayer:
 
     def __init__(self, cfg: MoEConfig, device="cuda", n_slots: Optional[int] = None,
                  n_halves: int = 2, compute_stream=None, copy_stream=None,
-                 copy_mode: int = B.MOE_COPY_SDMA, stitched: bool = False,
+                 copy_mode: int = B.MOE_COPY_KERNEL, stitched: bool = False,
                  allocate_halves: bool = True, fused_gather: bool = False):
         """stitched: each half is one virtual range over [the local-expert block | the half's own
         block], so merging the local experts copies nothing (page stitching, moe_vmm_*).

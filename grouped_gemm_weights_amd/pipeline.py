@@ -37,7 +37,7 @@ class MoEPipeline:
     block | half (l % 2)'s own block] (moe_vmm_*), so the merge copies nothing and the copy
     stream moves only the remote share; the halves' own blocks alternate between layers."""
 
-    def __init__(self, cfg: synth.MoEConfig, device="cuda", copy_mode: int = B.MOE_COPY_SDMA,
+    def __init__(self, cfg: synth.MoEConfig, device="cuda", copy_mode: int = B.MOE_COPY_KERNEL,
                  stitched: bool = False, fused_gather: bool = False):
         assert cfg.dtype == "bf16", "the pipeline runs the bf16 workloads"
         self.cfg = cfg

@@ -146,13 +146,26 @@ def test_merged_buffer_bytes_and_slot_map():
     # the runtime's copy and the library's copy kernel (one workgroup, and unbounded)
     # give the same bytes
     from grouped_gemm_weights_amd import binding as B
-    for mode in (B.MOE_COPY_ANY, B.copy_kernel_on(1), B.copy_kernel_on(0)):
+    for mode in (B.MOE_COPY_ANY, B.MOE_COPY_SDMA, B.copy_kernel_on(1), B.copy_kernel_on(0)):
         base.fill_(0)
         torch.cuda.synchronize()
         B.moe_merge_weights(L.local_pool, ids, L.wbufs[1], L.copy_stream, copy_mode=mode)
         B.moe_prefetch_layer(L.remote_pool, ids, L.wbufs[1], L.copy_stream, copy_mode=mode)
         L.synchronize()
         assert base.cpu().numpy()[: len(ids)].view(np.int16).tobytes() == merged.tobytes(), mode
+
+
+@pytest.mark.parametrize("mode", ["kernel", "any"])
+def test_fp32_odd_blocks_every_copy_path(mode):
+    """fp32 expert blocks of 3*5*3*4 = 180 bytes: not a multiple of 16, so the copy kernel
+    hands each run to the runtime copy; the layer still matches the oracle."""
+    from grouped_gemm_weights_amd import binding as B
+    cfg = synth.MoEConfig("f32_odd_blocks", T=24, H=5, I=3, E=6, k=2, dtype="f32", n_local=2,
+                          seed=21)
+    log(f"case {cfg.name} copy={mode}")
+    L = build_layer(cfg, copy_mode=B.MOE_COPY_KERNEL if mode == "kernel" else B.MOE_COPY_ANY)
+    _run(L)
+    check_full(cfg, L)
 
 
 # ----------------------------------------------------------------------------
