@@ -59,6 +59,9 @@ def parse():
                         "block into the half's virtual range so the merge copies nothing")
     p.add_argument("--cpu-sample-tokens", type=int, default=24)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-single-thread-tokens", type=int, default=2,
+                   help="tokens of the CPU sample also timed with the oracle held to one thread "
+                        "(0: skip)")
     p.add_argument("--calibrate", action="store_true",
                    help="run only a plain streaming kernel of known size (moe_residual_add over "
                         "1 GiB elements), the reference for scaling the HBM byte counters")
@@ -70,7 +73,7 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(cfg, L, n_tokens):
+def cpu_baseline(cfg, L, n_tokens, single_thread_tokens=0):
     """The oracle as it stands, on a bounded sample: routing and permutation of all tokens,
     the layer output of n_tokens tokens (every expert they route to is decoded once)."""
     import numpy as np
@@ -96,10 +99,44 @@ def cpu_baseline(cfg, L, n_tokens):
     O.moe_layer_tokens(x, logits, cfg.k, lambda e: blocks[e], cfg.H, cfg.I,
                        round_h=cfg.dtype == "bf16", tokens=tokens)
     dt = time.perf_counter() - t0
-    return {"value": round(len(tokens) / dt, 4), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(tokens)} of {cfg.T} tokens through the float64 oracle "
-                      f"(routing and permutation of all {cfg.T} tokens included), {dt:.1f} s"}
+    out = {"value": round(len(tokens) / dt, 4), "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"{len(tokens)} of {cfg.T} tokens through the float64 oracle "
+                     f"(routing and permutation of all {cfg.T} tokens included), {dt:.1f} s",
+           "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}
+    if single_thread_tokens > 0:
+        # the same oracle held to one BLAS thread, on a smaller sample of the same tokens
+        from threadpoolctl import threadpool_limits
+        few = tokens[:single_thread_tokens]
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            O.moe_layer_tokens(x, logits, cfg.k, lambda e: blocks[e], cfg.H, cfg.I,
+                               round_h=cfg.dtype == "bf16", tokens=few)
+            d1 = time.perf_counter() - t1
+        out["single_thread"] = {"value": round(len(few) / d1, 4), "unit": "tokens/s",
+                                "sample": f"{len(few)} tokens, layer output only, {d1:.1f} s"}
+    return out
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
+def input_digests(cfg, local, remote):
+    """SHA-256 of the seeded inputs: logits, activations and a strided sample of each weight
+    pool (every 2^20-th element), so two runs can be shown to have used the same data."""
+    from grouped_gemm_weights_amd import synth
+    d = {"logits": synth.digest(synth.logits(cfg)), "x": synth.digest(synth.activations(cfg))}
+    for name, pool in (("local_pool_sample", local), ("remote_pool_sample", remote)):
+        if pool is not None and pool.numel() > 0:
+            d[name] = synth.digest(pool.view(-1)[::1 << 20])
+    return d
 
 
 def bench_pipeline(args, cfg, dev, copy_mode):
@@ -174,6 +211,8 @@ def bench_pipeline(args, cfg, dev, copy_mode):
             "compute_pipelined_ms": round(mean(comp_pipe), 3), "compute_alone_ms": round(mean(C_alone), 3),
             "contention_slowdown": round(mean(comp_pipe) / mean(C_alone), 3),
             "layer_latency_ms": round(mean(Lat), 3),
+            "layer_latency_ms_median": round(float(np.median(Lat)), 3),
+            "layer_latency_ms_min": round(float(np.min(Lat)), 3),
             "max_compute_prefetch_ms": round(max(mean(C_alone), mean(P_alone)), 3),
         },
     }
@@ -389,6 +428,14 @@ def main():
     rp_ms = el("start", "rp_end")
     copy_ms = el("copy0", "copy1")
     layer_ms = el("start", "end")
+    per_step = lambda a, b: [B.moe_event_elapsed_ms(ev[a][i], ev[b][i]) for i in range(nev)]
+    layer_v = per_step("start", "end")
+    timing = {"layer_ms_median": round(float(np.median(layer_v)), 4),
+              "layer_ms_min": round(float(np.min(layer_v)), 4)}
+    if nch == 0:
+        gemm_v = per_step("gemm0", "gemm1")
+        timing.update({"grouped_swiglu_ms_median": round(float(np.median(gemm_v)), 4),
+                       "grouped_swiglu_ms_min": round(float(np.min(gemm_v)), 4)})
 
     counts = L.counts.cpu().numpy()
     n_active = int((counts > 0).sum())
@@ -437,14 +484,17 @@ def main():
         "breakdown_ms": {"route_permute": round(rp_ms, 4), "merge_prefetch_copy": round(copy_ms, 4),
                          "grouped_swiglu": round(gemm_ms, 4), "combine": round(combine_ms, 4),
                          "layer_events": round(layer_ms, 4)},
+        "timing": timing,
         "copy": {"bytes": copy_bytes, "experts": len(ids), "GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1)},
         "active_experts": n_active,
         "gemm_TFLOPs": round(gemm_tflops, 2),
     }
     if alt is not None:
         result["other_copy_engine"] = alt
+    result["inputs_sha256"] = input_digests(cfg, local, remote)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_sample_tokens,
+                                              args.cpu_single_thread_tokens)
     L.close()
     print(json.dumps(result), flush=True)
 
