@@ -22,6 +22,8 @@
 //
 // f32 path (tiny exact-check workloads): plain fp32 FMA kernels, one thread
 // per output element, fp32 throughout.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -121,7 +123,15 @@ __global__ __launch_bounds__(MOE_MAX_E) void plan_kernel(const int32_t* __restri
 // bf16 MFMA tile GEMM
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g * sigmoid(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) and the quotient
+// from the hardware exp2 and reciprocal (about 1 ulp each, so a few fp32 ulp in all).
+// Limits hold: g -> -inf gives e^-g = inf, 1 / inf = 0 and a (signed) zero; g -> +inf
+// gives g.  This runs once per output of the gate/up GEMM while its MFMA pipes wait, so
+// the libm exp and the IEEE division (dozens of instructions each) are avoided.
+__device__ __forceinline__ float silu_f32(float g) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // ---------------------------------------------------------------------------
 // Prefill work order: groups of kMGroup consecutive m-tiles sweep all n-tiles
@@ -377,32 +387,35 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
 #undef W_MFMA
 #undef W_STEP
 
-  // epilogue: element q of a 32x32 block sits at row (q/4)*8 + (lane/32)*4 + q%4, column lane%32
-#pragma unroll
-  for (int i = 0; i < MW; ++i)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = wm0 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-      if (r >= tile.rows) continue;
-      const int64_t orow = static_cast<int64_t>(tile.row0 + r) * ldo;
-      if (DUAL) {
-#pragma unroll
-        for (int jj = 0; jj < NJ / 2; ++jj) {
-          const int n = n0 + (MI ? wave * 32 : wn * 64 + jj * 32) + lrow;
-          if (n < N)
-            static_cast<uint16_t*>(out)[orow + n] =
-                f32_to_bf16(silu_f32(acc[i][jj][q]) * acc[i][NJ / 2 + jj][q]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int n = n0 + (MI ? wave * 64 : wn * 128) + j * 32 + lrow;
-          if (n >= N) continue;
-          if (OUT_BF16) static_cast<uint16_t*>(out)[orow + n] = f32_to_bf16(acc[i][j][q]);
-          else static_cast<float*>(out)[orow + n] = acc[i][j][q];
-        }
-      }
-    }
+  // epilogue: element q of a 32x32 block sits at row (q/4)*8 + (lane/32)*4 + q%4, column
+  // lane%32.  Offsets run from this lane's first output; a wave whose rows and columns all
+  // lie inside the tile and N (every full tile of an R1 layer) stores without checks.
+  constexpr int NO = DUAL ? NJ / 2 : NJ;  // 32-column output blocks per wave
+  const int r0 = wm0 + (lane >> 5) * 4;
+  const int cw = n0 + (MI ? (DUAL ? wave * 32 : wave * 64) : (DUAL ? wn * 64 : wn * 128));
+  const int64_t o0 = static_cast<int64_t>(tile.row0 + r0) * ldo + cw + lrow;
+  using OutT = typename std::conditional<DUAL || OUT_BF16, uint16_t, float>::type;
+  OutT* const obase = static_cast<OutT*>(out) + o0;
+#define W_EPI(CHECK)                                                                   \
+  do {                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < MW; ++i)                                     \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                   \
+      const int dr = i * 32 + (q >> 2) * 8 + (q & 3);                                  \
+      if ((CHECK) && r0 + dr >= tile.rows) continue;                                   \
+      OutT* const orow = obase + static_cast<int64_t>(dr) * ldo;                      \
+      _Pragma("unroll") for (int j = 0; j < NO; ++j) {                                 \
+        if ((CHECK) && cw + j * 32 + lrow >= N) continue;                              \
+        const float v = DUAL ? silu_f32(acc[i][j][q]) * acc[i][NO + j][q] : acc[i][j][q]; \
+        if constexpr (DUAL || OUT_BF16) orow[j * 32] = f32_to_bf16(v);                 \
+        else orow[j * 32] = v;                                                         \
+      }                                                                                \
+    }                                                                                  \
+  } while (0)
+  if (wm0 + MW * 32 <= tile.rows && cw + NO * 32 <= N)
+    W_EPI(false);
+  else
+    W_EPI(true);
+#undef W_EPI
 }
 
 template <bool DUAL, bool OUT_BF16, bool KFULL>
