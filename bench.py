@@ -187,6 +187,16 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     alg_bytes = cfg.E * eb + R * cfg.H * 6
     alg_flop = 6.0 * cfg.H * cfg.I * R
     gbps = alg_bytes / (gemm_ms * 1e-3) / 1e9
+    tflops = alg_flop / (gemm_ms * 1e-3) / 1e12
+    if alg_flop / alg_bytes < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": None, "kernel": "moe_grouped_swiglu, pipelined layers (with the copy running)",
+                 "avg_ms": round(gemm_ms, 4), "alg_bytes": alg_bytes, "alg_flop": alg_flop,
+                 "TFLOPs": round(tflops, 1), "GBps": round(gbps, 1)})
     return {
         "metric": "MoE layer tokens/s + grouped-GEMM % of HBM/MFMA roofline, R1 shape, 1 GPU",
         "value": round(cfg.T * args.steps / wall, 2), "unit": "tokens/s (through all layers)",
@@ -198,11 +208,7 @@ def bench_pipeline(args, cfg, dev, copy_mode):
                    "local_experts": cfg.n_local, "copy_engine": args.copy_mode,
                    "copy_blocks": args.copy_blocks if args.copy_mode == "kernel" else None,
                    "merge": args.merge, "gather": args.gather, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "moe_grouped_swiglu, pipelined layers (with the copy running)",
-                     "avg_ms": round(gemm_ms, 4), "alg_bytes": alg_bytes, "alg_flop": alg_flop,
-                     "TFLOPs": round(alg_flop / (gemm_ms * 1e-3) / 1e12, 1)},
+        "roofline": roof,
         "pipeline": {
             "prefetch_ms": round(mean(P_l), 3), "prefetch_alone_ms": round(mean(P_alone), 3),
             "copy_bytes": (cfg.E - (cfg.n_local if P.stitched else 0)) * eb,

@@ -84,6 +84,9 @@ CONFIGS = {
     # 6-layer pipeline, 4096 tokens per layer, dense stand-in block per layer
     "r1_pipeline_6x4096": MoEConfig("r1_pipeline_6x4096", T=4096, seed=505, layers=6,
                                     dense_standin=True, **_R1),
+    # 4-layer pipeline at 16384 tokens per layer: compute per layer well above the prefetch
+    "r1_pipeline_4x16384": MoEConfig("r1_pipeline_4x16384", T=16384, seed=606, layers=4,
+                                     dense_standin=True, **_R1),
 }
 # DWDP3: a 3-rank group holds 86 of the 256 experts locally and fetches 170
 _R1_3 = dict(_R1, n_local=86)

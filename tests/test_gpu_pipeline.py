@@ -1,11 +1,13 @@
-"""GPU parity of the 6-layer pipeline (4096 tokens per layer, R1 shape, dense
-stand-in block per layer, copy-stream prefetch into the double buffer).
+"""GPU parity of the multi-layer pipelines (R1 shape, dense stand-in block per
+layer, copy-stream prefetch into the double buffer): 6 layers of 4096 tokens
+(copy and stitched merge) and 4 layers of 16384 tokens (stitched merge, fused
+gather, as bench.py runs it).
 
 Per layer, the oracle is fed the GPU's own layer input (bf16), as the layer
 outputs are then compared one layer at a time; routing is checked bit-exactly
 on all tokens; the dense block, the MoE output and the residual are checked on
 sampled tokens.  Tokens are independent through every block, so the oracle
-also runs the whole 6-layer pipeline for the sampled tokens from the seeded
+also runs the whole pipeline for the sampled tokens from the seeded
 input and the final residual stream is compared end to end.
 
 The dense block output and the residual stream are stored in bf16 on both
@@ -37,6 +39,22 @@ def test_r1_pipeline_6x4096(stitched):
     cfg = synth.config("r1_pipeline_6x4096")
     log(f"case {cfg.name} stitched={stitched}")
     P = MoEPipeline(cfg, stitched=stitched)
+    try:
+        _check_pipeline(cfg, P, block_to_numpy)
+    finally:
+        P.close()
+        del P
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
+def test_r1_pipeline_4x16384():
+    """Four layers at 16384 tokens each, stitched merge: the same checks as above."""
+    from grouped_gemm_weights_amd.layer import block_to_numpy
+    from grouped_gemm_weights_amd.pipeline import MoEPipeline
+    cfg = synth.config("r1_pipeline_4x16384")
+    log(f"case {cfg.name} stitched=True")
+    P = MoEPipeline(cfg, stitched=True, fused_gather=True)
     try:
         _check_pipeline(cfg, P, block_to_numpy)
     finally:
