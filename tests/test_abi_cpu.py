@@ -88,3 +88,23 @@ def test_workspace_sizes(B):
     assert B.moe_permute_workspace_size(16384, 256, 8) >= 2 * 256 * 256 * 4
     R, I = 65536, 2048
     assert B.moe_grouped_swiglu_workspace_size(R, 256, 7168, I, B.MOE_BF16) >= R * I * 2
+
+
+def test_plain_c_caller(B, tmp_path):
+    """include/moe.h compiles as C99 with -Wall -Wextra -pedantic -Werror, a C program links
+    against libmoe.so, and its host-only entry points answer (tests/c_abi_consumer.c)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    exe = str(tmp_path / "c_abi_consumer")
+    libdir = os.path.dirname(LIB)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+           "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_abi_consumer.c"),
+           "-o", exe, "-L", libdir, "-lmoe", f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("ok moe-gfx950")
