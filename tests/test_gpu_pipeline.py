@@ -115,3 +115,52 @@ def _check_pipeline(cfg, P, block_to_numpy):
     log(f"end-to-end after {cfg.layers} layers: err/rms beyond {cfg.layers} bf16 spacings {e_end:.2e}, "
         f"normwise {norm_end:.2e}")
     assert e_end <= TOL["bf16"] and norm_end <= TOL["bf16"]
+
+
+def test_pipeline_event_timeline():
+    """The per-layer schedule (explainer, prefetch-schedule and per-layer latency panels) read
+    off the events of a pipelined pass over the 6 x 4096 workload: MoE block l starts only
+    after layer l's copy has ended; the stall measured around the wait matches the copy
+    timeline; copies are serial on their stream; a half is refilled only after the layer that
+    read it (two layers back) has finished; and layer latency covers the layer's compute."""
+    from grouped_gemm_weights_amd import binding as B
+    from grouped_gemm_weights_amd.pipeline import MoEPipeline
+    cfg = synth.config("r1_pipeline_6x4096")
+    log(f"case {cfg.name} event timeline")
+    P = MoEPipeline(cfg, stitched=True, fused_gather=True)
+    n = cfg.layers
+    keys = ("c0", "c1", "wait0", "wait1", "d0", "m1", "g1")
+    evs = []
+    try:
+        P.forward()                                   # warm-up
+        for _ in range(2):
+            ev = {k: [B.moe_event_create(True) for _ in range(n)] for k in keys}
+            evs.append(ev)
+            P.forward(ev)
+        P.synchronize()
+        assert P.L.read_status() == 0
+        tol = 0.05                                    # ms: event signalling across streams
+        for ev in evs:
+            t = lambda a, la, b, lb: B.moe_event_elapsed_ms(ev[a][la], ev[b][lb])
+            for l in range(n):
+                assert t("c1", l, "wait1", l) >= -tol, f"layer {l} ran before its weights landed"
+                stall = t("wait0", l, "wait1", l)
+                expect = max(0.0, t("wait0", l, "c1", l))
+                assert abs(stall - expect) <= 2 * tol, (l, stall, expect)
+                if l + 1 < n:
+                    assert t("c1", l, "c0", l + 1) >= -tol, f"copies of layers {l}, {l + 1} overlap"
+                if l >= 1 and l + 1 < n:
+                    assert t("m1", l - 1, "c0", l + 1) >= -tol, f"half refilled while layer {l - 1} read it"
+                if l >= 1:
+                    assert t("m1", l - 1, "m1", l) >= t("d0", l, "m1", l) - tol
+            lat = [t("m1", l - 1, "m1", l) for l in range(1, n)]
+            log("layer latency " + ", ".join(f"{v:.2f}" for v in lat) + " ms")
+    finally:
+        for ev in evs:
+            for lst in ev.values():
+                for e in lst:
+                    B.moe_event_destroy(e)
+        P.close()
+        del P
+        gc.collect()
+        torch.cuda.empty_cache()
