@@ -1,11 +1,14 @@
-// moe_grouped_swiglu: the grouped GEMM over the experts of the merged buffer,
-// with each expert's SwiGLU FFN, and moe_dense_gemm (the pipeline's dense
-// stand-in block), which runs the prefill tile loop on one weight matrix.
+// moe_grouped_swiglu: the grouped GEMM over the experts of the merged buffer
+// (DWDP explainer, contiguous-buffer panel: local and fetched experts feed one
+// grouped GEMM), with each expert's SwiGLU FFN, and moe_dense_gemm (the
+// pipeline's dense stand-in block), which runs the prefill tile loop on one
+// weight matrix.
 //
 // bf16 path (gfx950 MFMA, fp32 accumulate):
 //   1. plan:  one block turns offsets[] into a list of BM-row tiles
-//             (expert, first row, rows, slot), expert-major, and checks that
-//             every expert with rows has a slot in the merged buffer.
+//             (expert, first row, rows, slot), expert-major; prefill tiles go
+//             into two lists (full tiles, and short last tiles), and every
+//             expert with rows must have a slot in the merged buffer.
 //   2. gemm1: per (tile, column block): g = X Wg^T and u = X Wu^T share the
 //             A rows; the epilogue writes h = bf16(silu(g) * u).
 //   3. gemm2: per (tile, column block): y_perm = h Wd^T in fp32.
@@ -644,7 +647,7 @@ struct GemmStream {
 using Gemm1Stream = GemmStream<true, 4, 4>;
 using Gemm2Stream = GemmStream<false, 4, 4>;
 
-// prefill shapes: 128-row tiles
+// prefill shapes: 256-row tiles
 using Gemm1Prefill = GemmWide<true, false>;
 using Gemm2Prefill = GemmWide<false, false>;
 using DenseBf16 = GemmWide<false, true>;
