@@ -1,0 +1,55 @@
+"""bench.py's host-side bookkeeping, on synthetic counter files (no GPU): the HBM traffic
+record scales FETCH_SIZE / WRITE_SIZE by the calibration kernel's readings, sums only the
+grouped-GEMM kernels, and is ignored once the kernel source no longer matches it."""
+import csv
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _csv(d, sub, rows, counter):
+    os.makedirs(os.path.join(d, sub), exist_ok=True)
+    with open(os.path.join(d, sub, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, kib) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": kib})
+
+
+def test_traffic_record_scaling_and_source_guard(tmp_path, monkeypatch):
+    d = str(tmp_path / "prof")
+    n = 1 << 30
+    # the calibration kernel reads 6 GiB and writes 2 GiB; FETCH_SIZE reports half of it
+    _csv(d, "cal_fetch", [("moe::(anonymous namespace)::residual_kernel(...)", 3 * n / 1024)], "FETCH_SIZE")
+    _csv(d, "cal_write", [("moe::(anonymous namespace)::residual_kernel(...)", 2 * n / 1024)], "WRITE_SIZE")
+    gemm = "void moe::(anonymous namespace)::gemm_stream_kernel<true, true, 4, 4>(...)"
+    plan = "moe::(anonymous namespace)::plan_kernel(...)"
+    other = "moe::(anonymous namespace)::copy_kernel(...)"
+    # two dispatches of the GEMM (mean 1000 KiB fetched), one plan, and a kernel that must not count
+    _csv(d, "fetch_w", [(gemm, 900.0), (gemm, 1100.0), (plan, 2.0), (other, 1e9)], "FETCH_SIZE")
+    _csv(d, "write_w", [(gemm, 50.0), (gemm, 50.0), (plan, 1.0), (other, 1e9)], "WRITE_SIZE")
+    out = str(tmp_path / "traffic.json")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", out)
+    rec = bench.write_traffic(d, ["w"])
+    assert rec["calibration"]["fetch_scale"] == pytest.approx(2.0)
+    assert rec["calibration"]["write_scale"] == pytest.approx(1.0)
+    w = rec["workloads"]["w"]
+    assert w["read_bytes_per_call"] == round(1000 * 1024 * 2.0) + round(2 * 1024 * 2.0)
+    assert w["write_bytes_per_call"] == 50 * 1024 + 1024
+    assert w["hbm_bytes_per_call"] == w["read_bytes_per_call"] + w["write_bytes_per_call"]
+    assert w["per_kernel_per_launch"]["gemm_stream_kernel<true, true, 4, 4>"]["dispatches"] == 2
+    assert sorted(w["per_kernel_per_launch"]) == ["gemm_stream_kernel<true, true, 4, 4>", "plan_kernel"]
+    assert json.load(open(out)) == rec
+    # read back only while the kernel source is the one the counters were taken on
+    assert bench.traffic_from_profiles("w") == w
+    monkeypatch.setattr(bench, "_source_sha256", lambda: "0" * 64)
+    assert bench.traffic_from_profiles("w") is None
