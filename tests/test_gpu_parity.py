@@ -120,6 +120,34 @@ def test_all_tokens_one_expert_and_prefill_tiles():
     assert rel_err(out["y"], ref["y"]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
+def test_prefill_tile_modes_at_row_boundaries(fused):
+    """Expert row counts on both sides of every prefill tile mode (64/128/192-row column-split
+    tiles, full 256-row tiles, and a full tile plus a one-row tail), k = 1 so each count is
+    exact; I = 192 leaves the gate/up GEMM a partial column block, so the epilogue runs both
+    its unchecked (whole waves) and checked stores."""
+    counts = [64, 65, 128, 129, 192, 193, 256, 257]
+    T = sum(counts)
+    cfg = synth.MoEConfig("bf16_tile_modes", T=T, H=256, I=192, E=len(counts), k=1, dtype="bf16",
+                          n_local=3, seed=21)
+    log(f"case {cfg.name} fused={fused}")
+    L = build_layer(cfg, fused_gather=fused)
+    expert_of = np.repeat(np.arange(cfg.E), counts)
+    np.random.default_rng(22).shuffle(expert_of)       # tokens of an expert spread over the batch
+    logits = synth.logits(cfg)
+    logits[np.arange(T), expert_of] += 50.0
+    L.set_inputs(synth.activations(cfg), logits)
+    L.forward(half=0)
+    out = L.outputs()
+    assert out["status"] == 0
+    np.testing.assert_array_equal(out["counts"], counts)
+    check_routing(cfg, out, logits)
+    ref = O.moe_layer(synth.activations(cfg), logits, cfg.k, weights_fn(L), cfg.H, cfg.I, True)
+    e_yp, e_y = rel_err(out["y_perm"], ref["y_perm"]), rel_err(out["y"], ref["y"])
+    log(f"{cfg.name}: y_perm err/rms {e_yp:.3e}, y err/rms {e_y:.3e}")
+    assert e_yp <= TOL["bf16"] and e_y <= TOL["bf16"]
+
+
 def test_remote_pool_in_pinned_host_memory():
     cfg = synth.MoEConfig("bf16_host_remote", T=48, H=128, I=64, E=16, k=4, dtype="bf16",
                           n_local=4, seed=9)
