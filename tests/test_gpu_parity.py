@@ -148,6 +148,34 @@ def test_prefill_tile_modes_at_row_boundaries(fused):
     assert e_yp <= TOL["bf16"] and e_y <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
+def test_decode_tiles_at_row_boundaries(fused):
+    """Decode-path layer (at most 4 rows per expert on average) with expert row counts around
+    the 16-row stream tile (1, 15, 16, 17, 32, 33), k = 1; H = 320 and I = 192 give both stream
+    GEMMs a partial column block and a K tail (neither depth is a multiple of 128)."""
+    counts = [1, 15, 16, 17, 32, 33] + [0] * 26
+    T = sum(counts)
+    cfg = synth.MoEConfig("bf16_decode_tiles", T=T, H=320, I=192, E=len(counts), k=1,
+                          dtype="bf16", n_local=8, seed=23)
+    assert T <= 4 * cfg.E                      # the decode tiles are chosen
+    log(f"case {cfg.name} fused={fused}")
+    L = build_layer(cfg, fused_gather=fused)
+    expert_of = np.repeat(np.arange(cfg.E), counts)
+    np.random.default_rng(24).shuffle(expert_of)
+    logits = synth.logits(cfg)
+    logits[np.arange(T), expert_of] += 50.0
+    L.set_inputs(synth.activations(cfg), logits)
+    L.forward(half=1)
+    out = L.outputs()
+    assert out["status"] == 0
+    np.testing.assert_array_equal(out["counts"], counts)
+    check_routing(cfg, out, logits)
+    ref = O.moe_layer(synth.activations(cfg), logits, cfg.k, weights_fn(L), cfg.H, cfg.I, True)
+    e_yp, e_y = rel_err(out["y_perm"], ref["y_perm"]), rel_err(out["y"], ref["y"])
+    log(f"{cfg.name}: y_perm err/rms {e_yp:.3e}, y err/rms {e_y:.3e}")
+    assert e_yp <= TOL["bf16"] and e_y <= TOL["bf16"]
+
+
 def test_remote_pool_in_pinned_host_memory():
     cfg = synth.MoEConfig("bf16_host_remote", T=48, H=128, I=64, E=16, k=4, dtype="bf16",
                           n_local=4, seed=9)
