@@ -307,16 +307,17 @@ def write_traffic(prof_dir, workloads):
             "per_kernel_per_launch": per, "read_bytes_per_call": rd, "write_bytes_per_call": wr,
             "hbm_bytes_per_call": rd + wr,
             "commands": [
-                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {prof_dir}/fetch_{cfg} -o run -- "
+                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch_{cfg} -o run -- "
                 f"python3 bench.py --config {cfg} --steps 2 --warmup 1 --no-cpu-baseline",
-                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {prof_dir}/write_{cfg} -o run -- "
+                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write_{cfg} -o run -- "
                 f"python3 bench.py --config {cfg} --steps 2 --warmup 1 --no-cpu-baseline",
             ],
         }
     rec["calibration"]["commands"] = [
-        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {prof_dir}/cal_fetch -o run -- python3 bench.py --calibrate",
-        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {prof_dir}/cal_write -o run -- python3 bench.py --calibrate",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/cal_fetch -o run -- python3 bench.py --calibrate",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/cal_write -o run -- python3 bench.py --calibrate",
     ]
+    rec["output_dir"] = "$OUT: the directory the runs above wrote to (read by --write-traffic)"
     json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
     return rec
 
