@@ -18,6 +18,8 @@
 // workgroups: on one GPU, where the stand-in pull is an HBM-to-HBM copy, this
 // keeps it on a bounded set of compute units instead of spreading a runtime
 // copy kernel over the whole chip under a concurrent grouped GEMM.
+#include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "common.h"
@@ -47,6 +49,14 @@ __global__ void slot_fill_kernel(int32_t* slot_of, int E) {
 __global__ void slot_set_kernel(int32_t* slot_of, SlotChunk c) {
   const int i = threadIdx.x;
   if (i < c.n) slot_of[c.ids[i]] = c.first_slot + i;
+}
+
+// A caller's handling of a failed pull can be tested on a healthy device: with
+// MOE_INJECT_FAULT=<site> in the environment, the call at that site fails the way a failed
+// HIP call does, before it enqueues anything.
+bool injected_fault(const char* site) {
+  const char* v = std::getenv("MOE_INJECT_FAULT");
+  return v && std::strcmp(v, site) == 0;
 }
 
 int check_ids(const char* who, const int32_t* ids, int n, const moe_wbuf* dst) {
@@ -212,6 +222,8 @@ extern "C" int moe_prefetch_layer(const moe_pool* remote, const int32_t* ids_hos
                                   moe_wbuf* dst, moe_stream_t copy_stream, moe_event_t wait_free,
                                   moe_event_t ready, int copy_mode) {
   using namespace moe;
+  if (injected_fault("prefetch"))
+    return fail(MOE_ERR_HIP, "moe_prefetch_layer: fault injected (MOE_INJECT_FAULT=prefetch)");
   int rc = check_ids("moe_prefetch_layer", ids_host, n_ids, dst);
   if (rc) return rc;
   rc = check_pool("moe_prefetch_layer", remote, dst);

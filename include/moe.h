@@ -201,7 +201,9 @@ int moe_merge_weights(const moe_pool* local, const int32_t* ids_host, int n_ids,
  * alternate buffer while compute runs (DWDP explainer, "stay data-parallel"
  * and prefetch-schedule panels).  It does not write dst->slot_of.
  *   wait_free / ready / copy_mode as for moe_merge_weights.
- * Errors: as for moe_merge_weights.
+ * Errors: as for moe_merge_weights.  For tests of a caller's error handling,
+ * the environment variable MOE_INJECT_FAULT=prefetch makes the call return
+ * MOE_ERR_HIP at once, with nothing enqueued (the ready event is not recorded).
  */
 int moe_prefetch_layer(const moe_pool* remote, const int32_t* ids_host, int n_ids, moe_wbuf* dst,
                        moe_stream_t copy_stream, moe_event_t wait_free, moe_event_t ready,

@@ -108,3 +108,19 @@ def test_plain_c_caller(B, tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.startswith("ok moe-gfx950")
+
+
+def test_injected_prefetch_fault(B, monkeypatch):
+    """MOE_INJECT_FAULT=prefetch makes moe_prefetch_layer fail as a failed HIP call would,
+    before any argument is looked at (so no device memory is needed here); other sites and an
+    unset variable leave it alone."""
+    lib = ctypes.CDLL(LIB)
+    lib.moe_last_error.restype = ctypes.c_char_p
+    call = lambda: lib.moe_prefetch_layer(None, None, 0, None, None, None, None, 0)
+    monkeypatch.setenv("MOE_INJECT_FAULT", "prefetch")
+    assert call() == B.MOE_ERR_HIP
+    assert b"fault injected" in lib.moe_last_error()
+    monkeypatch.setenv("MOE_INJECT_FAULT", "merge")
+    assert call() == B.MOE_ERR_ARG                     # the real argument check runs again
+    monkeypatch.delenv("MOE_INJECT_FAULT")
+    assert call() == B.MOE_ERR_ARG

@@ -176,6 +176,63 @@ def test_decode_tiles_at_row_boundaries(fused):
     assert e_yp <= TOL["bf16"] and e_y <= TOL["bf16"]
 
 
+def test_late_prefetch_is_waited_for():
+    """The compute stream waits for the copy stream's ready event: with the half poisoned with
+    NaN and the copy stream held back by a spin kernel queued before the pull, the layer's
+    output is bit-identical to an undelayed run and the step's time grows by about the
+    delay (a missing or misplaced wait would read NaN weights)."""
+    cfg = synth.MoEConfig("bf16_late_prefetch", T=256, H=512, I=256, E=16, k=4, dtype="bf16",
+                          n_local=4, seed=25)
+    log(f"case {cfg.name}")
+    L = build_layer(cfg)
+    cs, ps = L.compute_stream, L.copy_stream
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed_step(delay_cycles):
+        base, _ = L.halves[0]
+        base.fill_(0xFF)                               # bf16 0xFFFF is NaN
+        torch.cuda.synchronize()
+        d0, d1, c0, c1 = ev(), ev(), ev(), ev()
+        d0.record(ps)
+        if delay_cycles:
+            with torch.cuda.stream(ps):
+                torch.cuda._sleep(delay_cycles)
+        d1.record(ps)
+        c0.record(cs)
+        L.forward(half=0)
+        c1.record(cs)
+        torch.cuda.synchronize()
+        return L.outputs(), d0.elapsed_time(d1), c0.elapsed_time(c1)
+
+    timed_step(0)                                      # warm-up
+    ref, _, t_base = timed_step(0)
+    assert ref["status"] == 0 and np.isfinite(ref["y"]).all()
+    late, delay, t_late = timed_step(20_000_000)
+    log(f"delay {delay:.2f} ms: step {t_base:.2f} -> {t_late:.2f} ms")
+    assert late["status"] == 0
+    assert late["y"].tobytes() == ref["y"].tobytes()
+    assert delay >= 2.0
+    assert t_late - t_base >= 0.5 * delay
+
+
+def test_injected_prefetch_fault_surfaces_and_recovers(monkeypatch):
+    """MOE_INJECT_FAULT=prefetch: the layer step raises the library's error instead of running
+    the GEMM on a half that was never filled; without it the next step is correct."""
+    from grouped_gemm_weights_amd import binding as B
+    cfg = synth.MoEConfig("bf16_fault", T=64, H=128, I=64, E=12, k=3, dtype="bf16", n_local=3,
+                          seed=27)
+    log(f"case {cfg.name}")
+    L = build_layer(cfg)
+    monkeypatch.setenv("MOE_INJECT_FAULT", "prefetch")
+    with pytest.raises(B.MoEError) as e:
+        L.forward(half=0)
+    assert e.value.code == B.MOE_ERR_HIP
+    monkeypatch.delenv("MOE_INJECT_FAULT")
+    L.synchronize()
+    L.forward(half=0)
+    check_full(cfg, L)
+
+
 def test_remote_pool_in_pinned_host_memory():
     cfg = synth.MoEConfig("bf16_host_remote", T=48, H=128, I=64, E=16, k=4, dtype="bf16",
                           n_local=4, seed=9)
