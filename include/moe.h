@@ -76,9 +76,11 @@ enum {
 #define MOE_COPY_SDMA 0 /* device-to-device copies on the SDMA engines, no compute units */
 #define MOE_COPY_ANY 1  /* let the runtime choose (it may use a copy kernel on the CUs) */
 /* The library's own streaming copy kernel for device-to-device runs, on at most n
- * workgroups of 1024 threads (n = 0: as many as the copy can use).  A small n keeps the
- * pull on a bounded set of compute units, so a grouped GEMM running beside it (one
- * workgroup per CU) keeps the rest; host-memory sources still use the runtime copy. */
+ * workgroups of 1024 threads (n = 0: as many as the copy can use).  A small n holds the
+ * pull to at most n compute units at a time, leaving the rest to a grouped GEMM running
+ * beside it (one workgroup per CU).  Each workgroup moves only ~20-25 GB/s, though, so on
+ * MI355X the unbounded copy (n = 0) is the faster choice even beside a GEMM.  Host-memory
+ * sources still use the runtime copy. */
 #define MOE_COPY_KERNEL 2
 #define MOE_COPY_KERNEL_ON(n) (MOE_COPY_KERNEL | ((n) << 8))
 
@@ -228,8 +230,8 @@ int moe_grouped_swiglu_workspace_size(int R, int E, int H, int I, moe_dtype dtyp
  *   status  device i32, may be NULL (MOE_STATUS_EXPERT_ABSENT when an expert
  *           with rows has slot -1; its rows are then left unwritten)
  * Errors: MOE_ERR_ARG for null pointers or sizes that disagree with w;
- * MOE_ERR_UNSUPPORTED when H or I is not a multiple of 8 or H*I >= 2^31;
- * MOE_ERR_WORKSPACE when ws_bytes is too small.
+ * MOE_ERR_UNSUPPORTED for E > MOE_MAX_E, H*I >= 2^31, or (MOE_BF16) H or I
+ * not a multiple of 8; MOE_ERR_WORKSPACE when ws_bytes is too small.
  */
 int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int R, int E, int H, int I,
                        moe_dtype dtype, const moe_wbuf* w, void* ws, size_t ws_bytes,
