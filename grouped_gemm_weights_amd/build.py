@@ -23,7 +23,7 @@ ARCH = "gfx950"
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
-    # packed fp32 instructions stay off (see the kernel notes in csrc/common.h)
+    # packed fp32 instructions (v_pk_*_f32) stay off: every kernel is built without them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -73,6 +73,7 @@ SwigluWs swiglu_ws(int64_t R, int E, int I, moe_dtype dt) {
 __global__ __launch_bounds__(MOE_MAX_E) void plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                          int e_begin, int e_end,
                                                          int BM, const int32_t* __restrict__ slot_of,
+                                                         int n_slots,
                                                          Tile* __restrict__ tiles,
                                                          int32_t* __restrict__ n_tiles,
                                                          int32_t* status) {
@@ -84,7 +85,9 @@ __global__ __launch_bounds__(MOE_MAX_E) void plan_kernel(const int32_t* __restri
     cnt = offsets[e + 1] - lo;
     if (cnt > 0) {
       slot = slot_of[e];
-      if (slot < 0) {
+      // a slot outside the merged buffer is treated as absent, never read
+      if (slot < 0 || slot >= n_slots) {
+        slot = -1;
         status_or(status, MOE_STATUS_EXPERT_ABSENT);
       } else if (BM < kWidePlanBM) {
         nh = (cnt + BM - 1) / BM;
@@ -671,6 +674,7 @@ __global__ __launch_bounds__(256) void gemm1_f32_kernel(const float* __restrict_
                                                         const int32_t* __restrict__ offsets, int E,
                                                         int e_begin, int e_end,
                                                         const int32_t* __restrict__ slot_of,
+                                                        int n_slots,
                                                         const char* __restrict__ wbase,
                                                         int64_t eb, int H, int I,
                                                         float* __restrict__ h, int32_t* status) {
@@ -681,7 +685,7 @@ __global__ __launch_bounds__(256) void gemm1_f32_kernel(const float* __restrict_
   const int e = expert_of_row(offsets, E, r);
   if (e < e_begin || e >= e_end) return;
   const int slot = slot_of[e];
-  if (slot < 0) {
+  if (slot < 0 || slot >= n_slots) {
     status_or(status, MOE_STATUS_EXPERT_ABSENT);
     return;
   }
@@ -701,6 +705,7 @@ __global__ __launch_bounds__(256) void gemm2_f32_kernel(const float* __restrict_
                                                         const int32_t* __restrict__ offsets, int E,
                                                         int e_begin, int e_end,
                                                         const int32_t* __restrict__ slot_of,
+                                                        int n_slots,
                                                         const char* __restrict__ wbase,
                                                         int64_t eb, int H, int I,
                                                         float* __restrict__ y_perm) {
@@ -711,7 +716,7 @@ __global__ __launch_bounds__(256) void gemm2_f32_kernel(const float* __restrict_
   const int e = expert_of_row(offsets, E, r);
   if (e < e_begin || e >= e_end) return;
   const int slot = slot_of[e];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= n_slots) return;
   const float* wd = reinterpret_cast<const float*>(wbase + static_cast<int64_t>(slot) * eb) +
                     2 * static_cast<int64_t>(H) * I + static_cast<int64_t>(o) * I;
   const float* hr = h + static_cast<int64_t>(r) * I;
@@ -775,11 +780,11 @@ int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
     hipLaunchKernelGGL(gemm1_f32_kernel, dim3(static_cast<unsigned>(ceil_div64(n1, 256))), dim3(256),
                        0, s, static_cast<const float*>(x_perm), a_index, a_div, offsets, E,
                        e_begin, e_end,
-                       w->slot_of, wbase, eb, H, I, static_cast<float*>(h), status);
+                       w->slot_of, w->n_slots, wbase, eb, H, I, static_cast<float*>(h), status);
     MOE_LAUNCH_CHECK("moe_grouped_swiglu: gemm1 f32");
     hipLaunchKernelGGL(gemm2_f32_kernel, dim3(static_cast<unsigned>(ceil_div64(n2, 256))), dim3(256),
                        0, s, static_cast<const float*>(h), offsets, E, e_begin, e_end, w->slot_of,
-                       wbase, eb, H, I, y_perm);
+                       w->n_slots, wbase, eb, H, I, y_perm);
     MOE_LAUNCH_CHECK("moe_grouped_swiglu: gemm2 f32");
     return MOE_OK;
   }
@@ -794,7 +799,7 @@ int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
   const int BM = decode ? 16 : Gemm1Prefill::BM;
   const int64_t grid_tiles = ceil_div64(R, BM) + std::min(E, R);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(MOE_MAX_E), 0, s, offsets, E, e_begin, e_end, BM,
-                     w->slot_of, tiles, n_tiles, status);
+                     w->slot_of, w->n_slots, tiles, n_tiles, status);
   MOE_LAUNCH_CHECK("moe_grouped_swiglu: plan");
 
   const int64_t HI2 = static_cast<int64_t>(H) * I * 2;  // bytes of one H x I bf16 matrix

@@ -228,7 +228,8 @@ int moe_grouped_swiglu_workspace_size(int R, int E, int H, int I, moe_dtype dtyp
  *   ws      device workspace of moe_grouped_swiglu_workspace_size() bytes
  *   y_perm  device f32[R][H]
  *   status  device i32, may be NULL (MOE_STATUS_EXPERT_ABSENT when an expert
- *           with rows has slot -1; its rows are then left unwritten)
+ *           with rows has slot -1, or a slot outside [0, w->n_slots), which is
+ *           never read; that expert's rows are then left unwritten)
  * Errors: MOE_ERR_ARG for null pointers or sizes that disagree with w;
  * MOE_ERR_UNSUPPORTED for E > MOE_MAX_E, H*I >= 2^31, or (MOE_BF16) H or I
  * not a multiple of 8; MOE_ERR_WORKSPACE when ws_bytes is too small.
@@ -270,6 +271,10 @@ int moe_grouped_swiglu_gathered(const void* x, const int32_t* src_of, int k, con
 /*
  * moe_combine -- the weighted un-permute:
  *   y[t] = sum_{j=0..k-1} topk_w[t][j] * y_perm[row_of[t*k + j]], summed in j order, f32.
+ * The pages give no combine rule of their own (like routing, the mixture only appears
+ * through the DWDP explainer's imbalance panels); this is the output of the plain top-k
+ * mixture of experts: each chosen expert's output weighted by its moe_route weight.  The
+ * fixed j order makes the sum reproducible run to run.
  *   y_perm device f32[T*k][H]; row_of device i32[T*k]; topk_w device f32[T][k];
  *   y device f32[T][H] (must not alias y_perm).
  * Errors: MOE_ERR_ARG for null pointers or bad sizes.

@@ -145,3 +145,108 @@ def check_sampled(cfg, L, tokens, layer: int = 0, x=None, logits=None, check_xpe
     log(f"{cfg.name}: {len(tokens)} sampled tokens: y err/rms {e_y:.3e}, y_perm err/rms {e_yp:.3e}")
     assert e_y <= tol and e_yp <= tol
     return out
+
+
+# ----------------------------------------------------------------------------
+# full-size checks: many rows, each expert's weights read back and decoded once
+# ----------------------------------------------------------------------------
+
+def expert_ffn_rows(weights_of, x_rows_by_expert, H, I, round_h=True, workers=8):
+    """The oracle's SwiGLU FFN of every expert e on its rows: {e: x rows} -> {e: float64 rows}.
+
+    Each expert's block is fetched once (``weights_of`` on this thread) and decoded and
+    multiplied on a worker thread, at most ``workers`` experts in flight (an R1 block decodes to
+    352 MB of float64)."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+
+    def work(bits, xr):
+        wg, wu, wd = O.expert_matrices(bits, H, I)
+        return O.swiglu_ffn(xr, wg, wu, wd, round_h)
+
+    out, pending = {}, {}
+    with threadpool_limits(limits=2), cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        for e in sorted(x_rows_by_expert):
+            if len(pending) >= workers:
+                done, _ = cf.wait(list(pending), return_when=cf.FIRST_COMPLETED)
+                for f in done:
+                    out[pending.pop(f)] = f.result()
+            pending[ex.submit(work, weights_of(e), x_rows_by_expert[e])] = e
+        for f in cf.as_completed(list(pending)):
+            out[pending[f]] = f.result()
+    return out
+
+
+def tile_boundary_rows(offsets, step: int = 32):
+    """Rows on both sides of every step-row boundary inside each expert's group, plus each
+    group's first and last row.  Every tile of the grouped GEMM starts at a multiple of its
+    32-row MFMA block from its expert's first row, so these include the first and last row of
+    every tile, whatever tile heights the kernel picks."""
+    rows = set()
+    off = np.asarray(offsets, dtype=np.int64)
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rows.update((lo, hi - 1))
+        for b in range(lo + step, hi, step):
+            rows.update((b - 1, b))
+    return sorted(rows)
+
+
+def check_rows(cfg, L, rows, tokens, layer: int = 0, x=None, logits=None, check_xperm=True,
+               workers=8):
+    """Routing and permutation bit-exact on all tokens (and x_perm bitwise when built); y_perm
+    on the given rows plus every row of the given tokens, and y on the given tokens, against
+    the oracle's per-expert FFN of the rows (x read through the oracle's permutation).
+    ``rows`` may be a function of the oracle's offsets (e.g. ``tile_boundary_rows``)."""
+    out = L.outputs()
+    assert out["status"] == 0, f"device status {out['status']}"
+    x = synth.activations(cfg, layer) if x is None else x
+    logits = synth.logits(cfg, layer) if logits is None else logits
+    idx, w, src_of, row_of = check_routing(cfg, out, logits)
+    if check_xperm:
+        assert np.array_equal(out["x_perm"], np.asarray(x)[src_of // cfg.k])
+    offsets = O.expert_offsets(O.expert_counts(idx, cfg.E))
+    if callable(rows):
+        rows = rows(offsets)
+    tokens = [int(t) for t in tokens]
+    tok_rows = [int(row_of[t * cfg.k + j]) for t in tokens for j in range(cfg.k)]
+    rows = np.array(sorted(set(int(r) for r in rows) | set(tok_rows)), dtype=np.int64)
+    e_of = np.searchsorted(offsets, rows, side="right") - 1
+    xa = np.asarray(x)
+    by_e = {int(e): rows[e_of == e] for e in np.unique(e_of)}
+    ffn = expert_ffn_rows(weights_fn(L), {e: xa[src_of[r] // cfg.k] for e, r in by_e.items()},
+                          cfg.H, cfg.I, round_h=cfg.dtype == "bf16", workers=workers)
+    ref = np.empty((len(rows), cfg.H))
+    pos = {int(r): i for i, r in enumerate(rows)}
+    for e, r in by_e.items():
+        ref[[pos[int(v)] for v in r]] = ffn[e]
+    tol = TOL[cfg.dtype]
+    e_yp = rel_err(out["y_perm"][rows], ref)
+    # y of the tokens: the oracle's combine over their k rows, in j order
+    yp_tok = ref[[pos[r] for r in tok_rows]]
+    y_ref = O.combine(yp_tok, np.arange(len(tok_rows)), w[tokens], cfg.k)
+    e_y = rel_err(out["y"][tokens], y_ref)
+    log(f"{cfg.name}: y_perm on {len(rows)} rows of {len(by_e)} experts: err/rms {e_yp:.3e}; "
+        f"y on {len(tokens)} tokens: err/rms {e_y:.3e} (tol {tol})")
+    assert e_yp <= tol and e_y <= tol
+    return out, len(rows)
+
+
+def tokens_layer(weights_of, x_rows, logits_rows, k, H, I, round_h=True, workers=8):
+    """The oracle's layer output for a set of token rows: O.route of their logits, each chosen
+    expert's FFN on its tokens (expert_ffn_rows: one decode per expert, experts in parallel),
+    then O.combine over the k slots in j order.  The same value as O.moe_layer_tokens, which
+    walks the experts one at a time."""
+    xr = O.decode(x_rows)
+    idx, w = O.route(logits_rows, k)
+    n = xr.shape[0]
+    flat = idx.ravel()
+    by_e = {int(e): np.nonzero(flat == e)[0] for e in np.unique(flat)}
+    ffn = expert_ffn_rows(weights_of, {e: xr[a // k] for e, a in by_e.items()}, H, I, round_h,
+                          workers)
+    yp = np.empty((n * k, H))
+    for e, a in by_e.items():
+        yp[a] = ffn[e]
+    return O.combine(yp, np.arange(n * k), w, k)

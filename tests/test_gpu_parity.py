@@ -12,8 +12,8 @@ import gc
 import numpy as np
 import pytest
 
-from moe_cases import (O, TOL, build_layer, check_full, check_routing, check_sampled, log,
-                       rel_err, synth, weights_fn)
+from moe_cases import (O, TOL, build_layer, check_full, check_routing, check_rows, check_sampled,
+                       log, rel_err, synth, tile_boundary_rows, weights_fn)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +118,55 @@ def test_all_tokens_one_expert_and_prefill_tiles():
     idx, w, src_of, row_of = check_routing(cfg, out, logits)
     ref = O.moe_layer(synth.activations(cfg), logits, cfg.k, weights_fn(L), cfg.H, cfg.I, True)
     assert rel_err(out["y"], ref["y"]) <= TOL["bf16"]
+
+
+def _tied_logits(cfg, seed):
+    """Logits with ties everywhere: N(0,1) rounded to multiples of 0.5, plus rows of one repeated
+    value, rows of +0.0 and -0.0 mixed (equal under the routing order), rows where a run of
+    equal values straddles the k-th place, and a row of -0.0 with one +0.0 at the end."""
+    rng = np.random.default_rng(seed)
+    L = (np.round(rng.standard_normal((cfg.T, cfg.E)) * 2.0) / 2.0).astype(np.float32)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    L[0, :] = 1.5                                              # all equal: ids 0..k-1, w = 1/k
+    L[1, :] = np.where(rng.random(E) < 0.5, 0.0, -0.0).astype(np.float32)
+    L[2, :] = -0.0
+    L[2, E - 1] = 0.0                                          # +0 == -0: still ids 0..k-1
+    L[3, :] = -1.0
+    L[3, E // 2:] = 2.0                                        # equal top values from the middle
+    L[4, :] = 0.5
+    L[4, rng.choice(E, size=max(1, k // 2), replace=False)] = 3.0   # a run straddling place k
+    for t in range(5, min(T, 12)):                             # signed zeros in quantised rows
+        z = rng.choice(E, size=E // 3, replace=False)
+        L[t, z] = np.where(rng.random(z.size) < 0.5, 0.0, -0.0)
+    return L
+
+
+@pytest.mark.parametrize("E,k,H,I", [(256, 8, 64, 32), (8, 2, 64, 32), (1000, 8, 64, 32)],
+                         ids=["E256_k8", "E8_k2", "E1000_k8"])
+def test_routing_ties_and_signed_zeros(E, k, H, I):
+    """Quantised logits tie constantly; the order (logit desc, id asc, +0 == -0) must pick the
+    oracle's ids bit-exactly, and counts, offsets and the permutation with them.  The whole
+    layer is checked too."""
+    cfg = synth.MoEConfig(f"bf16_ties_E{E}_k{k}", T=200, H=H, I=I, E=E, k=k, dtype="bf16",
+                          n_local=E // 4, seed=31 + E)
+    log(f"case {cfg.name}")
+    L = build_layer(cfg)
+    logits = _tied_logits(cfg, 32 + E)
+    L.set_inputs(synth.activations(cfg), logits)
+    L.forward(half=0)
+    out = L.outputs()
+    assert out["status"] == 0
+    idx, w, src_of, row_of = check_routing(cfg, out, logits)
+    np.testing.assert_array_equal(out["idx"][0], np.arange(k))
+    np.testing.assert_array_equal(out["idx"][2], np.arange(k))
+    assert np.max(np.abs(out["w"][0] - 1.0 / k)) <= 2e-7
+    ties = sum(int(np.sum(logits[t] == logits[t, idx[t, -1]]) > 1) for t in range(cfg.T))
+    log(f"{cfg.name}: {ties} of {cfg.T} tokens have a tie at the k-th place")
+    assert ties > cfg.T // 4
+    ref = O.moe_layer(synth.activations(cfg), logits, cfg.k, weights_fn(L), cfg.H, cfg.I, True)
+    e_y = rel_err(out["y"], ref["y"])
+    log(f"{cfg.name}: y err/rms {e_y:.3e}")
+    assert e_y <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
@@ -304,6 +353,16 @@ def test_status_nonfinite_logit_and_absent_expert():
     L.expert_compute(0)
     st = L.read_status()
     assert st & B.MOE_STATUS_EXPERT_ABSENT and not st & B.MOE_STATUS_NONFINITE_LOGIT
+    # a slot map entry past the merged buffer is reported as absent and never read
+    L.status.zero_()
+    L.fill_half(0, ids)
+    L.synchronize()
+    _, slot_of = L.halves[0]
+    slot_of[missing] = L.n_slots + 5
+    torch.cuda.synchronize()
+    L.expert_compute(0)
+    st = L.read_status()
+    assert st == B.MOE_STATUS_EXPERT_ABSENT
 
 
 # ----------------------------------------------------------------------------
@@ -321,7 +380,9 @@ def test_r1_decode_t64(stitched):
     L = build_layer(cfg, stitched=stitched)
     try:
         _run(L)
-        check_sampled(cfg, L, _sample(cfg.T, 8, 1))
+        # every token and every one of the T*k rows
+        _, n = check_rows(cfg, L, range(cfg.R), range(cfg.T))
+        assert n == cfg.R
         # a second step on the other half of the double buffer gives the same bits
         y0 = L.y.clone()
         torch.cuda.synchronize()
@@ -400,11 +461,13 @@ def test_fused_gather_tiny_fp32():
 
 
 def test_r1_prefill_t16384_fused_gather():
+    """As bench.py runs it (stitched merge, gather on load): the first and last row of every
+    tile and every 32-row block boundary of every expert, and 64 sampled tokens."""
     cfg = synth.config("r1_prefill_t16384")
     L = build_layer(cfg, stitched=True, fused_gather=True)
     try:
         L.forward(half=0, remote="all")
-        check_sampled(cfg, L, _sample(cfg.T, 4, 13), check_xperm=False)
+        check_rows(cfg, L, tile_boundary_rows, _sample(cfg.T, 64, 13), check_xperm=False)
     finally:
         L.close()
 
@@ -428,16 +491,24 @@ def test_stitched_halves_small():
         L.close()
 
 
-def test_r1_prefill_t8192_zipf():
+@pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
+def test_r1_prefill_t8192_zipf(fused):
+    """Skewed routing: a few experts with thousands of rows (full tiles), many with a handful
+    (short tiles).  Every tile's first and last row, every 32-row block boundary, and 64
+    sampled tokens."""
     cfg = synth.config("r1_prefill_t8192_zipf")
-    log(f"case {cfg.name}")
-    L = _run(build_layer(cfg))
-    out = check_sampled(cfg, L, _sample(cfg.T, 6, 2))
-    log(f"active experts {int((out['counts'] > 0).sum())}, max rows {int(out['counts'].max())}")
+    log(f"case {cfg.name} fused={fused}")
+    L = build_layer(cfg, stitched=fused, fused_gather=fused)
+    try:
+        _run(L)
+        out, n = check_rows(cfg, L, tile_boundary_rows, _sample(cfg.T, 64, 2), check_xperm=not fused)
+        log(f"active experts {int((out['counts'] > 0).sum())}, max rows {int(out['counts'].max())}")
+    finally:
+        L.close()
 
 
 def test_r1_prefill_t16384():
     cfg = synth.config("r1_prefill_t16384")
     log(f"case {cfg.name}")
     L = _run(build_layer(cfg), remote="all")
-    check_sampled(cfg, L, _sample(cfg.T, 6, 3))
+    check_rows(cfg, L, tile_boundary_rows, _sample(cfg.T, 64, 3))

@@ -6,7 +6,7 @@ gather, as bench.py runs it).
 Per layer, the oracle is fed the GPU's own layer input (bf16), as the layer
 outputs are then compared one layer at a time; routing is checked bit-exactly
 on all tokens; the dense block, the MoE output and the residual are checked on
-sampled tokens.  Tokens are independent through every block, so the oracle
+16 sampled tokens.  Tokens are independent through every block, so the oracle
 also runs the whole pipeline for the sampled tokens from the seeded
 input and the final residual stream is compared end to end.
 
@@ -22,7 +22,7 @@ import gc
 import numpy as np
 import pytest
 
-from moe_cases import O, TOL, W_TOL, log, rel_err, rel_err_bf16, synth
+from moe_cases import O, TOL, W_TOL, log, rel_err, rel_err_bf16, synth, tokens_layer
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -64,8 +64,9 @@ def test_r1_pipeline_4x16384():
         torch.cuda.empty_cache()
 
 
-def _check_pipeline(cfg, P, block_to_numpy):
-    tokens = sorted(np.random.default_rng(6).choice(cfg.T, size=4, replace=False).tolist())
+def _check_pipeline(cfg, P, block_to_numpy, n_tokens=16):
+    tokens = sorted(np.random.default_rng(6).choice(cfg.T, size=n_tokens, replace=False).tolist())
+    n = len(tokens)
     cap = []
 
     def hook(l):
@@ -78,7 +79,10 @@ def _check_pipeline(cfg, P, block_to_numpy):
     P.synchronize()
     assert P.L.read_status() == 0
     x_final = _bits(P.x)
-    specs = []
+    # the oracle's own chain from the seeded input, run layer by layer beside the per-layer
+    # checks (routing depends on the seeded logits only, so both use the same experts and each
+    # expert's weights are decoded once per layer)
+    xo = O.decode(synth.activations(cfg, 0)[tokens])
     for l in range(cfg.layers):
         c = cap[l]
         logits = synth.logits(cfg, l)
@@ -91,29 +95,36 @@ def _check_pipeline(cfg, P, block_to_numpy):
         def weights_of(e, l=l):
             blk = P.locals[l][e] if e < cfg.n_local else P.remotes[l][e - cfg.n_local]
             return block_to_numpy(blk)
-        # dense stand-in on the GPU's own x_l
+        # dense stand-in on the GPU's own x_l, and on the oracle's chain
         a_ref = O.dense_standin(c["x"][tokens], w_attn)
         e_a = rel_err_bf16(O.decode(c["a"][tokens]), a_ref)
-        # MoE block on the GPU's own A_l
-        ref = O.moe_layer_tokens(c["a"], logits, cfg.k, weights_of, cfg.H, cfg.I, True, tokens)
-        e_y = rel_err(c["y"][tokens], ref["y"])
+        ao = O.dense_standin(xo, w_attn)
+        # MoE block: the GPU's own A_l rows (first n) and the chain's rows (last n), one call
+        both = tokens_layer(weights_of, np.concatenate([O.decode(c["a"][tokens]), ao]),
+                            np.concatenate([logits[tokens], logits[tokens]]), cfg.k, cfg.H, cfg.I)
+        e_y = rel_err(c["y"][tokens], both[:n])
         # residual on the GPU's own x_l and y_l: round to nearest bf16 of the sum
         x_next = cap[l + 1]["x"] if l + 1 < cfg.layers else x_final
         res_ref = O.residual(c["x"][tokens], c["y"][tokens])
         e_r = rel_err_bf16(O.decode(x_next[tokens]), res_ref)
-        log(f"layer {l}: dense err/rms {e_a:.2e}, moe err/rms {e_y:.2e}, residual err/rms {e_r:.2e}")
+        xo = O.residual(xo, both[n:])
+        log(f"layer {l}: {n} tokens: dense err/rms {e_a:.2e}, moe err/rms {e_y:.2e}, "
+            f"residual err/rms {e_r:.2e}")
         assert e_a <= TOL["bf16"] and e_y <= TOL["bf16"] and e_r <= TOL["bf16"]
-        specs.append(dict(logits=logits[tokens], w_attn=w_attn, weights_of=weights_of))
-    # end to end from the seeded input, oracle only
-    x0 = synth.activations(cfg, 0)[tokens]
-    out = O.pipeline(x0, specs, cfg.k, cfg.H, cfg.I)
-    ref_end = out[-1]["x_out"]
+    # end to end against the oracle's chain from the seeded input
     got_end = O.decode(x_final[tokens])
-    # the residual stream is re-rounded to bf16 after every layer: one boundary per layer
-    e_end = rel_err_bf16(got_end, ref_end, roundings=cfg.layers)
-    norm_end = float(np.sqrt(np.mean((got_end - ref_end) ** 2) / np.mean(ref_end ** 2)))
-    log(f"end-to-end after {cfg.layers} layers: err/rms beyond {cfg.layers} bf16 spacings {e_end:.2e}, "
-        f"normwise {norm_end:.2e}")
+    # every layer re-rounds the residual stream to bf16: two correct implementations can land
+    # on opposite sides of one rounding boundary per layer (at |x| ~ 4 one spacing is 2^-5,
+    # ~2.8 % of the stream's RMS), so the max-norm bound allows one spacing per layer; the
+    # plain max|err|/RMS is logged beside it and the normwise error is bounded directly
+    e_end = rel_err_bf16(got_end, xo, roundings=cfg.layers)
+    plain_end = rel_err(got_end, xo)
+    norm_end = float(np.sqrt(np.mean((got_end - xo) ** 2) / np.mean(xo ** 2)))
+    diff = np.abs(got_end - xo)
+    flips = float(np.mean(diff > 0))
+    log(f"end-to-end after {cfg.layers} layers, {n} tokens: plain max|err|/RMS {plain_end:.2e}, "
+        f"beyond {cfg.layers} bf16 spacings {e_end:.2e}, normwise {norm_end:.2e}, "
+        f"elements differing {flips:.2%}")
     assert e_end <= TOL["bf16"] and norm_end <= TOL["bf16"]
 
 

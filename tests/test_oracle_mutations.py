@@ -88,9 +88,30 @@ def _wrong_offsets(counts):
     return np.concatenate([np.cumsum(counts), [int(np.sum(counts))]]).astype(np.int32)   # inclusive scan
 
 
+def _wrong_dense_transposed(x, w_attn):
+    return O.round_to_bf16(O.decode(x) @ O.decode(w_attn))          # W used as in x out
+
+
+def _wrong_dense_unrounded(x, w_attn):
+    return O.decode(x) @ O.decode(w_attn).T                         # bf16 rounding dropped
+
+
+def _wrong_residual_unrounded(x, y):
+    return O.decode(x) + np.asarray(y, dtype=np.float64)            # bf16 rounding dropped
+
+
+def _wrong_residual_y_rounded(x, y):
+    return O.round_to_bf16(O.decode(x) + O.round_to_bf16(y))       # y rounded before the add
+
+
+def _wrong_tokens_no_round_h(x, logits, k, weights_of, H, I, round_h, tokens):
+    return _orig["moe_layer_tokens"](x, logits, k, weights_of, H, I, False, tokens)   # round_h dropped
+
+
 _orig = {name: getattr(O, name) for name in
          ["silu", "route", "permutation", "gather_rows", "expert_matrices", "swiglu_ffn",
-          "combine", "round_to_bf16", "expert_offsets"]}
+          "combine", "round_to_bf16", "expert_offsets", "dense_standin", "residual",
+          "moe_layer_tokens"]}
 
 MUTATIONS = [
     ("silu", _wrong_silu),
@@ -103,6 +124,11 @@ MUTATIONS = [
     ("combine", _wrong_combine),
     ("round_to_bf16", _wrong_round),
     ("expert_offsets", _wrong_offsets),
+    ("dense_standin", _wrong_dense_transposed),
+    ("dense_standin", _wrong_dense_unrounded),
+    ("residual", _wrong_residual_unrounded),
+    ("residual", _wrong_residual_y_rounded),
+    ("moe_layer_tokens", _wrong_tokens_no_round_h),
 ]
 
 PINS = [getattr(P, n) for n in dir(P) if n.startswith("test_")]

@@ -412,3 +412,76 @@ def test_synth_determinism_and_stats():
     c = O.expert_counts(idx, z.E)
     assert c.max() > 0.8 * z.T            # one hot expert takes most tokens
     assert (c > 0).sum() < z.E            # skew leaves experts idle
+
+
+# ----------------------------------------------------------------------------
+# pipeline blocks: dense stand-in and residual, against index loops with an
+# independent rounding to bf16 (exact rational arithmetic, not the oracle's
+# frexp/rint route)
+# ----------------------------------------------------------------------------
+
+def brute_bf16(v):
+    """Nearest bf16 value of a float by exact rational comparison of its two neighbours,
+    ties to the one with an even last significand bit (normal range only)."""
+    from fractions import Fraction
+    if v == 0.0:
+        return v
+    m, e = math.frexp(abs(v))                 # |v| = m 2^e, m in [0.5, 1)
+    step = Fraction(2) ** (e - 8)             # bf16 keeps 8 significant bits
+    q = Fraction(abs(v)) / step
+    lo = math.floor(q)
+    rem = q - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return math.copysign(float(lo * step), v)
+
+
+def test_brute_bf16_agrees_with_torch_cast():
+    torch = pytest.importorskip("torch")
+    v = np.random.default_rng(5).standard_normal(3000).astype(np.float32) * 7
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert [brute_bf16(float(a)) for a in v] == ref.tolist()
+
+
+def test_dense_standin_index_loops():
+    """A = bf16(x W^T) with W stored out x in, W deliberately not symmetric."""
+    rng = np.random.default_rng(41)
+    M, H = 5, 12
+    x = synth.to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((H, H)) / math.sqrt(H)).astype(np.float32))
+    xd, wd = O.decode(x).tolist(), O.decode(w).tolist()
+    want = [[brute_bf16(sum(xd[m][c] * wd[n][c] for c in range(H))) for n in range(H)]
+            for m in range(M)]
+    got = O.dense_standin(x, w)
+    np.testing.assert_array_equal(got, np.array(want))
+    # the stand-in output lies on the bf16 grid
+    np.testing.assert_array_equal(O.round_to_bf16(got), got)
+
+
+def test_residual_index_loops():
+    """x_next = bf16(x + y): x bf16 bits, y float32, one rounding of the exact sum."""
+    rng = np.random.default_rng(43)
+    x = synth.to_bf16_bits(rng.standard_normal((4, 9)).astype(np.float32))
+    y = (rng.standard_normal((4, 9)) * 0.3).astype(np.float32)
+    y[0, 0] = 2.0 ** -9                           # x + y lands next to a rounding boundary
+    xd = O.decode(x)
+    want = [[brute_bf16(float(xd[i, j]) + float(y[i, j])) for j in range(9)] for i in range(4)]
+    np.testing.assert_array_equal(O.residual(x, y), np.array(want))
+
+
+def test_layer_tokens_round_h_matches_dense_bruteforce():
+    """The per-token path with the bf16 h rounding (the path the full-size GPU checks use)
+    against the dense every-expert evaluation with the same rounding."""
+    cfg = synth.MoEConfig("bf16_small_tok", T=24, H=32, I=16, E=10, k=3, dtype="bf16",
+                          n_local=3, seed=79, zipf_s=1.1, rho_seed=80)
+    x = synth.activations(cfg)
+    L = synth.logits(cfg)
+    blocks = synth.pool_np(cfg, 0, range(cfg.E))
+    ref = dense_bruteforce_layer(x, L, cfg.k, blocks, cfg.H, cfg.I, True)
+    tok = [0, 3, 7, 11, 23]
+    rt = O.moe_layer_tokens(x, L, cfg.k, lambda e: blocks[e], cfg.H, cfg.I, True, tok)
+    scale = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(rt["y"] - ref[tok])) <= 1e-12 * scale
+    # and without the rounding it is the unrounded definition, a measurably different value
+    unr = dense_bruteforce_layer(x, L, cfg.k, blocks, cfg.H, cfg.I, False)
+    assert np.max(np.abs(unr[tok] - ref[tok])) > 1e-6 * scale
