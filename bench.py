@@ -57,11 +57,15 @@ def parse():
     p.add_argument("--merge", choices=["copy", "stitched"], default="stitched",
                    help="copy the local experts into each merged half, or stitch the local "
                         "block into the half's virtual range so the merge copies nothing")
-    p.add_argument("--cpu-sample-tokens", type=int, default=24)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-single-thread-tokens", type=int, default=2,
-                   help="tokens of the CPU sample also timed with the oracle held to one thread "
-                        "(0: skip)")
+    p.add_argument("--cpu-single-thread-tokens", type=int, default=8,
+                   help="tokens of the layer also run through the CPU bulk path with one BLAS "
+                        "thread (0: skip)")
+    p.add_argument("--workloads", default="r1_prefill_t8192_zipf,r1_prefill_t16384,r1_pipeline_6x4096",
+                   help="other workloads timed in the same run and reported under 'workloads' "
+                        "('none': only the headline)")
+    p.add_argument("--workload-steps", type=int, default=10)
+    p.add_argument("--pipeline-steps", type=int, default=3)
     p.add_argument("--calibrate", action="store_true",
                    help="run only a plain streaming kernel of known size (moe_residual_add over "
                         "1 GiB elements), the reference for scaling the HBM byte counters")
@@ -73,13 +77,14 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(cfg, L, n_tokens, single_thread_tokens=0):
-    """The oracle as it stands, on a bounded sample: routing and permutation of all tokens,
-    the layer output of n_tokens tokens (every expert they route to is decoded once)."""
+def cpu_baseline_bulk(cfg, blocks, y_gpu, single_thread_tokens=0):
+    """The oracle's bulk path over the whole layer: route, stable permutation, gather, then per
+    expert (one expert's weights decoded at a time, from host copies of the bytes the GPU read)
+    float32 products with h rounded to bf16 as the GPU stores it, and the float32 combine.
+    The GPU's output of the same step is compared with it (max|err|/RMS)."""
     import numpy as np
     from oracle import moe as O
     from grouped_gemm_weights_amd import synth
-    from grouped_gemm_weights_amd.layer import block_to_numpy
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -87,34 +92,30 @@ def cpu_baseline(cfg, L, n_tokens, single_thread_tokens=0):
         threads = 1
     x = synth.activations(cfg)
     logits = synth.logits(cfg)
-    tokens = list(range(min(n_tokens, cfg.T)))
-    # expert blocks are host copies taken before the clock starts (the oracle reads host memory)
-    idx, _ = O.route(logits[tokens], cfg.k)
-    blocks = {int(e): block_to_numpy(L.expert_block(int(e))) for e in np.unique(idx)}
+    rh = cfg.dtype == "bf16"
     t0 = time.perf_counter()
-    idx_all, w_all = O.route(logits, cfg.k)
-    counts = O.expert_counts(idx_all, cfg.E)
-    O.expert_offsets(counts)
-    O.permutation(idx_all, cfg.E)
-    O.moe_layer_tokens(x, logits, cfg.k, lambda e: blocks[e], cfg.H, cfg.I,
-                       round_h=cfg.dtype == "bf16", tokens=tokens)
+    res = O.moe_layer(x, logits, cfg.k, lambda e: blocks[e], cfg.H, cfg.I, round_h=rh,
+                      dtype=np.float32)
     dt = time.perf_counter() - t0
-    out = {"value": round(len(tokens) / dt, 4), "unit": "tokens/s", "cores": int(threads),
+    ref = res["y"].astype(np.float64)
+    err = float(np.max(np.abs(np.asarray(y_gpu, np.float64) - ref)) / np.sqrt(np.mean(ref ** 2)))
+    out = {"value": round(cfg.T / dt, 4), "unit": "tokens/s", "cores": int(threads),
            "kind": "oracle",
-           "sample": f"{len(tokens)} of {cfg.T} tokens through the float64 oracle "
-                     f"(routing and permutation of all {cfg.T} tokens included), {dt:.1f} s",
-           "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}
+           "sample": f"the whole {cfg.T}-token layer, route to combine, through the oracle's bulk "
+                     f"float32 path ({len(blocks)} experts decoded one at a time), {dt:.1f} s",
+           "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
+           "gpu_vs_cpu_max_err_over_rms": round(err, 6)}
     if single_thread_tokens > 0:
-        # the same oracle held to one BLAS thread, on a smaller sample of the same tokens
         from threadpoolctl import threadpool_limits
-        few = tokens[:single_thread_tokens]
+        n = min(single_thread_tokens, cfg.T)
         with threadpool_limits(limits=1):
             t1 = time.perf_counter()
-            O.moe_layer_tokens(x, logits, cfg.k, lambda e: blocks[e], cfg.H, cfg.I,
-                               round_h=cfg.dtype == "bf16", tokens=few)
+            O.moe_layer(x[:n], logits[:n], cfg.k, lambda e: blocks[e], cfg.H, cfg.I, round_h=rh,
+                        dtype=np.float32)
             d1 = time.perf_counter() - t1
-        out["single_thread"] = {"value": round(len(few) / d1, 4), "unit": "tokens/s",
-                                "sample": f"{len(few)} tokens, layer output only, {d1:.1f} s"}
+        out["single_thread"] = {"value": round(n / d1, 4), "unit": "tokens/s",
+                                "sample": f"the same path on the first {n} tokens, one BLAS "
+                                          f"thread, {d1:.1f} s"}
     return out
 
 
@@ -177,8 +178,15 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     P.forward_serial(sev)
     torch.cuda.synchronize()
     C_alone = [el(sev["d0"][l], sev["m1"][l]) for l in range(n)]
-    P.close()
     P_alone = [el(sev["c0"][l], sev["c1"][l]) for l in range(n)]
+    copy_bytes = (cfg.E - (cfg.n_local if P.stitched else 0)) * synth.expert_block_bytes(cfg)
+    P.close()
+    for e in [e for ev in evs + [sev] for lst in ev.values() for e in lst]:
+        B.moe_event_destroy(e)
+    del P
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
     mean = lambda v: float(np.mean(v))
     H = 1.0 - sum(stall) / sum(P_l)
     eb = synth.expert_block_bytes(cfg)
@@ -211,8 +219,8 @@ def bench_pipeline(args, cfg, dev, copy_mode):
         "roofline": roof,
         "pipeline": {
             "prefetch_ms": round(mean(P_l), 3), "prefetch_alone_ms": round(mean(P_alone), 3),
-            "copy_bytes": (cfg.E - (cfg.n_local if P.stitched else 0)) * eb,
-            "copy_GBps": round((cfg.E - (cfg.n_local if P.stitched else 0)) * eb / (mean(P_l) * 1e-3) / 1e9, 1),
+            "copy_bytes": copy_bytes,
+            "copy_GBps": round(copy_bytes / (mean(P_l) * 1e-3) / 1e9, 1),
             "stall_ms": round(mean(stall), 3), "hidden_fraction": round(H, 4),
             "compute_pipelined_ms": round(mean(comp_pipe), 3), "compute_alone_ms": round(mean(C_alone), 3),
             "contention_slowdown": round(mean(comp_pipe) / mean(C_alone), 3),
@@ -220,6 +228,17 @@ def bench_pipeline(args, cfg, dev, copy_mode):
             "layer_latency_ms_median": round(float(np.median(Lat)), 3),
             "layer_latency_ms_min": round(float(np.min(Lat)), 3),
             "max_compute_prefetch_ms": round(max(mean(C_alone), mean(P_alone)), 3),
+            "sum_compute_prefetch_ms": round(mean(C_alone) + mean(P_alone), 3),
+            # how close the layer comes to max(C, P), the per-layer latency panel's ideal
+            "latency_over_max_compute_prefetch": round(mean(Lat) / max(mean(C_alone), mean(P_alone)), 3),
+            # share of the prefetch's own time that the overlap actually saves:
+            # (C_alone + P_alone - L) / P_alone; 1 = fully hidden at no cost, 0 = serial
+            "overlap_efficiency": round((mean(C_alone) + mean(P_alone) - mean(Lat)) / mean(P_alone), 3),
+            # one GPU moves per layer the weights the GEMMs read, the dense block's weight and
+            # the pull twice (a read and a write of the same HBM): its time at 8 TB/s
+            "hbm_floor_ms": round((cfg.E * eb + cfg.H * cfg.H * 2 + 2 * copy_bytes) / HBM_PEAK_GBPS / 1e6, 3),
+            "hidden_fraction_definition": "1 - stall/prefetch: time the compute stream waits for "
+                                          "the copy, not the slowdown the copy causes",
         },
     }
 
@@ -336,11 +355,9 @@ def main():
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from grouped_gemm_weights_amd import binding as B
     from grouped_gemm_weights_amd import synth
-    from grouped_gemm_weights_amd.layer import MoELayer
 
     cfg = synth.config(args.config)
     dev = torch.device("cuda:0")
@@ -350,6 +367,64 @@ def main():
     if cfg.layers != 1:
         print(json.dumps(bench_pipeline(args, cfg, dev, copy_mode)), flush=True)
         return
+    host_blocks = {}
+    result = bench_layer(args, cfg, dev, copy_mode, args.steps, args.warmup, args.alt_steps,
+                         headline=True, host_blocks=host_blocks)
+    # the other R1 workloads in the same run, each timed as above (default options), so the
+    # prefill MFMA fractions and the pipeline's overlap figures sit beside the headline
+    names = [w for w in args.workloads.split(",") if w and w != "none"]
+    if names:
+        wl = {}
+        for name in names:
+            c = synth.config(name)
+            t0 = time.perf_counter()
+            if c.layers == 1:
+                r = bench_layer(args, c, dev, copy_mode, args.workload_steps, 2, 0)
+                wl[name] = layer_summary(r)
+            else:
+                pa = argparse.Namespace(**vars(args))
+                pa.steps, pa.warmup = args.pipeline_steps, 1
+                wl[name] = pipeline_summary(bench_pipeline(pa, c, dev, copy_mode))
+            wl[name]["bench_wall_s"] = round(time.perf_counter() - t0, 1)
+            print(f"[bench] {name} done in {wl[name]['bench_wall_s']} s", file=sys.stderr, flush=True)
+        result["workloads"] = wl
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_bulk(cfg, host_blocks, result.pop("_y"),
+                                                   args.cpu_single_thread_tokens)
+    result.pop("_y", None)
+    print(json.dumps(result), flush=True)
+
+
+def layer_summary(r):
+    """The figures of a single-layer record that matter beside the headline."""
+    keep = ("value", "unit", "ms_per_step", "roofline", "breakdown_ms", "timing", "copy",
+            "active_experts", "gemm_TFLOPs", "hbm_frac", "mfma_frac")
+    out = {k: r[k] for k in keep if k in r}
+    out["config"] = {k: r["config"][k] for k in ("tokens", "remote_fetch", "merge", "gather",
+                                                  "copy_engine")}
+    return out
+
+
+def pipeline_summary(r):
+    out = {"value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"],
+           "steps": r["steps"], "roofline": r["roofline"]}
+    out.update(r["pipeline"])
+    out["config"] = {k: r["config"][k] for k in ("layers", "tokens", "merge", "gather",
+                                                  "copy_engine")}
+    return out
+
+
+def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=False,
+                host_blocks=None):
+    """One MoE layer step timed over ``steps`` steps; returns its record.  With ``headline``
+    the record also carries the input digests and the layer output (for the CPU comparison),
+    and host copies of the routed experts' blocks are left in ``host_blocks``."""
+    import numpy as np
+    import torch
+    from grouped_gemm_weights_amd import binding as B
+    from grouped_gemm_weights_amd import synth
+    from grouped_gemm_weights_amd.layer import MoELayer, block_to_numpy
+
     L = MoELayer(cfg, device=dev, copy_mode=copy_mode, stitched=args.merge == "stitched",
                  fused_gather=args.gather == "fused")
     local = synth.pool_torch(cfg, 0, 0, cfg.n_local, dev)
@@ -358,7 +433,7 @@ def main():
     L.set_inputs(synth.activations(cfg), synth.logits(cfg))
     cs, ps = L.compute_stream, L.copy_stream
 
-    nev = args.steps
+    nev = steps
     mk = lambda: [B.moe_event_create(True) for _ in range(nev)]
     ev = {k: mk() for k in ("start", "rp_end", "gemm0", "gemm1", "end", "copy0", "copy1")}
     nch = max(0, args.chunks)
@@ -396,17 +471,17 @@ def main():
             B.moe_event_record(ev["end"][i], cs)
         return ids
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         ids = step(i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert L.read_status() == 0, "device status set during the benchmark"
     alt = None
-    if args.alt_steps > 0:
+    if alt_steps > 0:
         # the same step with the other copy path, for comparison (not the reported value)
         alt_name = "sdma" if args.copy_mode == "any" else "any"
         L.copy_mode = B.MOE_COPY_SDMA if alt_name == "sdma" else B.MOE_COPY_ANY
@@ -414,10 +489,10 @@ def main():
             step(i, False)
         torch.cuda.synchronize()
         ta = time.perf_counter()
-        for i in range(args.alt_steps):
+        for i in range(alt_steps):
             step(i, False)
         torch.cuda.synchronize()
-        alt_s = (time.perf_counter() - ta) / args.alt_steps
+        alt_s = (time.perf_counter() - ta) / alt_steps
         alt = {"copy_engine": alt_name,
                "ms_per_step": round(alt_s * 1e3, 3), "tokens_per_s": round(cfg.T / alt_s, 1)}
         L.copy_mode = copy_mode
@@ -443,6 +518,9 @@ def main():
         gemm_v = per_step("gemm0", "gemm1")
         timing.update({"grouped_swiglu_ms_median": round(float(np.median(gemm_v)), 4),
                        "grouped_swiglu_ms_min": round(float(np.min(gemm_v)), 4)})
+    for lst in list(ev.values()) + [l for g in gev for l in g.values()]:
+        for e in lst:
+            B.moe_event_destroy(e)
 
     counts = L.counts.cpu().numpy()
     n_active = int((counts > 0).sum())
@@ -471,12 +549,12 @@ def main():
 
     result = {
         "metric": "MoE layer tokens/s + grouped-GEMM % of HBM/MFMA roofline, R1 shape, 1 GPU",
-        "value": round(cfg.T * args.steps / wall, 2),
+        "value": round(cfg.T * steps / wall, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -495,15 +573,24 @@ def main():
         "copy": {"bytes": copy_bytes, "experts": len(ids), "GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1)},
         "active_experts": n_active,
         "gemm_TFLOPs": round(gemm_tflops, 2),
+        "hbm_frac": round(gemm_gbps / HBM_PEAK_GBPS, 4),
+        "mfma_frac": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
     }
     if alt is not None:
         result["other_copy_engine"] = alt
-    result["inputs_sha256"] = input_digests(cfg, local, remote)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_sample_tokens,
-                                              args.cpu_single_thread_tokens)
+    if headline:
+        result["inputs_sha256"] = input_digests(cfg, local, remote)
+        result["_y"] = L.y.detach().cpu().numpy()
+        if host_blocks is not None and not args.no_cpu_baseline:
+            # host copies of the routed experts, taken outside every timed region
+            for e in np.nonzero(counts)[0]:
+                host_blocks[int(e)] = block_to_numpy(L.expert_block(int(e)))
     L.close()
-    print(json.dumps(result), flush=True)
+    del L, local, remote
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    return result
 
 
 if __name__ == "__main__":

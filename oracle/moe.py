@@ -197,9 +197,12 @@ def merge(pools: Sequence[tuple], ids: Sequence[int]) -> np.ndarray:
 # SwiGLU experts
 # ----------------------------------------------------------------------------
 
-def expert_matrices(block: np.ndarray, H: int, I: int):
-    """Split one expert block into float64 (Wg [I,H], Wu [I,H], Wd [H,I]), stored out x in."""
+def expert_matrices(block: np.ndarray, H: int, I: int, dtype=np.float64):
+    """Split one expert block into (Wg [I,H], Wu [I,H], Wd [H,I]), stored out x in, as float64
+    (or ``dtype``: float32 for the bulk CPU path; bf16 and fp32 values convert exactly)."""
     b = decode(block).ravel()
+    if dtype != np.float64:
+        b = b.astype(dtype)
     if b.size != 3 * H * I:
         raise ValueError("expert block has the wrong size")
     wg = b[: H * I].reshape(I, H)
@@ -214,44 +217,49 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_ffn(x_rows: np.ndarray, wg, wu, wd, round_h: bool) -> np.ndarray:
+def swiglu_ffn(x_rows: np.ndarray, wg, wu, wd, round_h: bool, dtype=np.float64) -> np.ndarray:
     """SwiGLU FFN of one expert on rows x[n, H]: (silu(x Wg^T) * (x Wu^T)) Wd^T.
 
     With ``round_h`` the activation h is stored as bf16 (round to nearest
     even) before the down projection, as a bf16 workload stores it.
+    ``dtype`` is the arithmetic type: float64 (the definition), or float32
+    for the bulk CPU path (the same steps with float32 matrix products).
     """
-    x = decode(x_rows)
+    x = decode(x_rows).astype(dtype)
     g = x @ wg.T
     u = x @ wu.T
     h = silu(g) * u
     if round_h:
         h = round_to_bf16(h)
-    return h @ wd.T
+    return (h.astype(dtype) @ wd.T).astype(dtype)
 
 
 def grouped_swiglu(x_perm: np.ndarray, offsets: np.ndarray,
                    weights_of: Callable[[int], np.ndarray], H: int, I: int,
-                   round_h: bool) -> np.ndarray:
-    """y_perm[r] = FFN_e(x_perm[r]) for the rows r of every expert group e (float64)."""
+                   round_h: bool, dtype=np.float64) -> np.ndarray:
+    """y_perm[r] = FFN_e(x_perm[r]) for the rows r of every expert group e (float64, or
+    ``dtype``), one expert's weights decoded at a time."""
     xp = decode(x_perm)
     R = xp.shape[0]
-    y = np.zeros((R, H), dtype=np.float64)
+    y = np.zeros((R, H), dtype=dtype)
     E = len(offsets) - 1
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
-        wg, wu, wd = expert_matrices(weights_of(e), H, I)
-        y[lo:hi] = swiglu_ffn(xp[lo:hi], wg, wu, wd, round_h)
+        wg, wu, wd = expert_matrices(weights_of(e), H, I, dtype)
+        y[lo:hi] = swiglu_ffn(xp[lo:hi], wg, wu, wd, round_h, dtype)
     return y
 
 
-def combine(y_perm: np.ndarray, row_of: np.ndarray, w: np.ndarray, k: int) -> np.ndarray:
-    """y[t] = sum_{j=0..k-1} w[t,j] * y_perm[row_of[t*k + j]], summed in j order (float64)."""
-    yp = np.asarray(y_perm, dtype=np.float64)
-    w = np.asarray(w, dtype=np.float64)
+def combine(y_perm: np.ndarray, row_of: np.ndarray, w: np.ndarray, k: int,
+            dtype=np.float64) -> np.ndarray:
+    """y[t] = sum_{j=0..k-1} w[t,j] * y_perm[row_of[t*k + j]], summed in j order (float64, or
+    ``dtype``)."""
+    yp = np.asarray(y_perm, dtype=dtype)
+    w = np.asarray(w, dtype=dtype)
     T = w.shape[0]
-    y = np.zeros((T, yp.shape[1]), dtype=np.float64)
+    y = np.zeros((T, yp.shape[1]), dtype=dtype)
     for j in range(k):
         y += w[:, j:j + 1] * yp[np.asarray(row_of)[np.arange(T) * k + j]]
     return y
@@ -263,16 +271,19 @@ def combine(y_perm: np.ndarray, row_of: np.ndarray, w: np.ndarray, k: int) -> np
 
 def moe_layer(x: np.ndarray, logits: np.ndarray, k: int,
               weights_of: Callable[[int], np.ndarray], H: int, I: int,
-              round_h: bool) -> Dict[str, np.ndarray]:
-    """Route -> counts/offsets -> permutation -> gather -> grouped SwiGLU -> combine."""
+              round_h: bool, dtype=np.float64) -> Dict[str, np.ndarray]:
+    """Route -> counts/offsets -> permutation -> gather -> grouped SwiGLU -> combine.
+
+    ``dtype`` float32 gives the bulk CPU path: the same steps, with the expert
+    products and the combine in float32 (routing and permutation are exact)."""
     T, E = np.asarray(logits).shape
     idx, w = route(logits, k)
     counts = expert_counts(idx, E)
     offsets = expert_offsets(counts)
     row_of, src_of = permutation(idx, E)
     x_perm = gather_rows(x, src_of, k)
-    y_perm = grouped_swiglu(x_perm, offsets, weights_of, H, I, round_h)
-    y = combine(y_perm, row_of, w, k)
+    y_perm = grouped_swiglu(x_perm, offsets, weights_of, H, I, round_h, dtype)
+    y = combine(y_perm, row_of, w, k, dtype)
     return dict(idx=idx, w=w, counts=counts, offsets=offsets, row_of=row_of,
                 src_of=src_of, x_perm=x_perm, y_perm=y_perm, y=y)
 

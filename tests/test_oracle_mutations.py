@@ -141,6 +141,7 @@ def _run_pins():
         params = {
             "test_route_matches_bruteforce": [(50, 8, 2), (30, 256, 8)],
             "test_counts_offsets_permutation_bruteforce": [(17, 5, 2), (33, 256, 8)],
+            "test_bulk_float32_path_matches_the_definition": [("tiny_fp32_t64",), ("bf16_small",)],
         }.get(fn.__name__, [()])
         for args in params:
             try:

@@ -485,3 +485,29 @@ def test_layer_tokens_round_h_matches_dense_bruteforce():
     # and without the rounding it is the unrounded definition, a measurably different value
     unr = dense_bruteforce_layer(x, L, cfg.k, blocks, cfg.H, cfg.I, False)
     assert np.max(np.abs(unr[tok] - ref[tok])) > 1e-6 * scale
+
+
+# ----------------------------------------------------------------------------
+# the bulk float32 path (the CPU baseline) against the float64 definition
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_fp32_t64", "bf16_small"])
+def test_bulk_float32_path_matches_the_definition(name):
+    if name == "tiny_fp32_t64":
+        cfg = synth.config(name)
+    else:
+        cfg = synth.MoEConfig(name, T=48, H=64, I=40, E=12, k=4, dtype="bf16", n_local=3, seed=83)
+    x, L = synth.activations(cfg), synth.logits(cfg)
+    blocks = synth.pool_np(cfg, 0, range(cfg.E))
+    rh = cfg.dtype == "bf16"
+    ref = O.moe_layer(x, L, cfg.k, lambda e: blocks[e], cfg.H, cfg.I, rh)
+    got = O.moe_layer(x, L, cfg.k, lambda e: blocks[e], cfg.H, cfg.I, rh, dtype=np.float32)
+    for key in ("idx", "w", "counts", "offsets", "row_of", "src_of"):
+        np.testing.assert_array_equal(got[key], ref[key])
+    assert got["y"].dtype == np.float32 and got["y_perm"].dtype == np.float32
+    rms = np.sqrt(np.mean(ref["y"] ** 2))
+    # float32 products over H terms; with h rounded to bf16 an element of h may land on the
+    # other side of a rounding boundary (one bf16 spacing), which the 2e-2 bound absorbs
+    tol = 1e-5 if not rh else 2e-2
+    assert np.max(np.abs(got["y"] - ref["y"])) <= tol * rms
+    assert np.max(np.abs(got["y"] - ref["y"])) > 0          # it really ran in float32
