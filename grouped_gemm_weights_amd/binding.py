@@ -29,7 +29,8 @@ def copy_kernel_on(n_blocks: int) -> int:
 
 # Every symbol include/moe.h declares (checked by the CPU tests).
 EXPORTS = (
-    "moe_route", "moe_permute_workspace_size", "moe_permute", "moe_merge_weights",
+    "moe_route", "moe_permute_workspace_size", "moe_permute", "moe_permute_noalloc",
+    "moe_merge_weights",
     "moe_prefetch_layer", "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu",
     "moe_grouped_swiglu_range", "moe_grouped_swiglu_gathered",
     "moe_combine", "moe_dense_gemm", "moe_residual_add", "moe_event_create",
@@ -66,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "moe_route": [P, I, I, I, P, P, P, P],
         "moe_permute_workspace_size": [I, I, I, PSZ],
         "moe_permute": [P, I, I, I, P, I, I, P, P, P, P, P, P, SZ, P, P],
+        "moe_permute_noalloc": [P, I, I, I, P, I, I, P, P, P, P, P, P, P],
         "moe_merge_weights": [ctypes.POINTER(MoePool), P, I, ctypes.POINTER(MoeWbuf), P, P, P, I],
         "moe_prefetch_layer": [ctypes.POINTER(MoePool), P, I, ctypes.POINTER(MoeWbuf), P, P, P, I],
         "moe_grouped_swiglu_workspace_size": [I, I, I, I, I, PSZ],
@@ -157,6 +159,14 @@ def moe_permute(topk_idx, T, E, k, x, H, dtype, counts, offsets, row_of, src_of,
     _check("moe_permute", lib.moe_permute(ptr(topk_idx), T, E, k, ptr(x), H, dtype, ptr(counts),
                                           ptr(offsets), ptr(row_of), ptr(src_of), ptr(x_perm),
                                           ptr(ws), ws_bytes, ptr(status), stream_handle(stream)))
+
+
+def moe_permute_noalloc(topk_idx, T, E, k, x, H, dtype, counts, offsets, row_of, src_of, x_perm,
+                        status=None, stream=None):
+    _check("moe_permute_noalloc",
+           lib.moe_permute_noalloc(ptr(topk_idx), T, E, k, ptr(x), H, dtype, ptr(counts),
+                                   ptr(offsets), ptr(row_of), ptr(src_of), ptr(x_perm),
+                                   ptr(status), stream_handle(stream)))
 
 
 def moe_merge_weights(local: MoePool, ids: Sequence[int], dst: MoeWbuf, stream=None,

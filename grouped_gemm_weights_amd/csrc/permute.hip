@@ -14,6 +14,8 @@
 //              the running position across batches.  No atomics decide an
 //              order, so the permutation is the stable counting sort.
 //  4. gather:  x_perm[r] = x[src_of[r] / k] with 16-byte vector copies.
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -229,23 +231,34 @@ extern "C" int moe_permute_workspace_size(int T, int E, int k, size_t* bytes) {
   return MOE_OK;
 }
 
-extern "C" int moe_permute(const int32_t* topk_idx, int T, int E, int k, const void* x, int H,
-                           moe_dtype dtype, int32_t* counts, int32_t* offsets, int32_t* row_of,
-                           int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes,
-                           int32_t* status, moe_stream_t stream) {
-  using namespace moe;
+namespace moe {
+
+// The allocation-free variant's workspace: chunk_counts and chunk_base, each at most
+// kMaxChunks x MOE_MAX_E int32, i.e. the most any (T, E, k) the kernels accept can need
+// (2 MiB; every GPU the library runs on holds its own copy until the process ends).  Host
+// code must not pass this name to a kernel (on the host it is only a stand-in for the
+// symbol): every use goes through the per-device address from hipGetSymbolAddress.
+constexpr size_t kPermuteScratchBytes = 2 * size_t{kMaxChunks} * MOE_MAX_E * sizeof(int32_t);
+__device__ __align__(256) char permute_scratch[kPermuteScratchBytes];
+
+namespace {
+
+int permute_impl(const char* who, const int32_t* topk_idx, int T, int E, int k, const void* x,
+                 int H, moe_dtype dtype, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                 int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes, int32_t* status,
+                 moe_stream_t stream) {
   if (T < 0 || E < 1 || k < 1 || H < 1 || (dtype != MOE_F32 && dtype != MOE_BF16))
-    return fail(MOE_ERR_ARG, "moe_permute: bad sizes T=%d E=%d k=%d H=%d", T, E, k, H);
-  if (E > MOE_MAX_E) return fail(MOE_ERR_UNSUPPORTED, "moe_permute: E=%d above %d", E, MOE_MAX_E);
+    return fail(MOE_ERR_ARG, "%s: bad sizes T=%d E=%d k=%d H=%d", who, T, E, k, H);
+  if (E > MOE_MAX_E) return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d above %d", who, E, MOE_MAX_E);
   const int64_t R64 = static_cast<int64_t>(T) * k;
-  if (R64 > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_permute: T*k too large");
+  if (R64 > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k too large", who);
   const int R = static_cast<int>(R64);
   if (!counts || !offsets || (R > 0 && (!topk_idx || !row_of || !src_of)))
-    return fail(MOE_ERR_ARG, "moe_permute: null pointer");
-  if (x_perm && R > 0 && !x) return fail(MOE_ERR_ARG, "moe_permute: x_perm given without x");
+    return fail(MOE_ERR_ARG, "%s: null pointer", who);
+  if (x_perm && R > 0 && !x) return fail(MOE_ERR_ARG, "%s: x_perm given without x", who);
   const size_t need = permute_ws_bytes(R, E);
   if (need > 0 && (!ws || ws_bytes < need))
-    return fail(MOE_ERR_WORKSPACE, "moe_permute: workspace %zu < %zu bytes", ws_bytes, need);
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
 
   hipStream_t s = as_stream(stream);
   const Chunking ch = R > 0 ? chunking(R) : Chunking{64, 0};
@@ -274,4 +287,57 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int E, int k, const v
     MOE_LAUNCH_CHECK("moe_permute: gather launch");
   }
   return MOE_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of permute_scratch on the current device, looked up once per device.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  MOE_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_permute_noalloc: device %d above %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    MOE_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(permute_scratch)));
+    if (!p) return fail(MOE_ERR_HIP, "moe_permute_noalloc: no device address for the scratch array");
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_permute(const int32_t* topk_idx, int T, int E, int k, const void* x, int H,
+                           moe_dtype dtype, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                           int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes,
+                           int32_t* status, moe_stream_t stream) {
+  return moe::permute_impl("moe_permute", topk_idx, T, E, k, x, H, dtype, counts, offsets, row_of,
+                           src_of, x_perm, ws, ws_bytes, status, stream);
+}
+
+extern "C" int moe_permute_noalloc(const int32_t* topk_idx, int T, int E, int k, const void* x,
+                                   int H, moe_dtype dtype, int32_t* counts, int32_t* offsets,
+                                   int32_t* row_of, int32_t* src_of, void* x_perm, int32_t* status,
+                                   moe_stream_t stream) {
+  using namespace moe;
+  if (T < 0 || E < 1 || k < 1)
+    return fail(MOE_ERR_ARG, "moe_permute_noalloc: bad sizes T=%d E=%d k=%d", T, E, k);
+  if (E > MOE_MAX_E) return fail(MOE_ERR_UNSUPPORTED, "moe_permute_noalloc: E=%d above %d", E, MOE_MAX_E);
+  const int64_t R = static_cast<int64_t>(T) * k;
+  if (R > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_permute_noalloc: T*k too large");
+  const size_t need = permute_ws_bytes(R, E);
+  if (need > kPermuteScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "moe_permute_noalloc: needs %zu scratch bytes, above the "
+                "%zu the library holds", need, kPermuteScratchBytes);
+  void* scratch = nullptr;
+  const int rc = scratch_on_current_device(&scratch);
+  if (rc) return rc;
+  return permute_impl("moe_permute_noalloc", topk_idx, T, E, k, x, H, dtype, counts, offsets,
+                      row_of, src_of, x_perm, scratch, kPermuteScratchBytes, status, stream);
 }

@@ -170,6 +170,23 @@ int moe_permute(const int32_t* topk_idx, int T, int E, int k, const void* x, int
                 moe_stream_t stream);
 
 /*
+ * moe_permute_noalloc -- moe_permute with no workspace argument and no allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Its kernels use a file-scope device array of
+ * 2 MiB (the most moe_permute's workspace can need for any T, k and E <= MOE_MAX_E) that
+ * each GPU holds until the process ends; its address is looked up once per device.
+ * Every call on a GPU shares that array: calls that overlap on one GPU (on different
+ * streams, or from several threads) race and must be ordered by the caller.  Nothing in it
+ * needs clearing: each call writes all of it that it reads.
+ * Arguments and outputs: as moe_permute, without ws / ws_bytes.
+ * Errors: as moe_permute; MOE_ERR_WORKSPACE if a size needed more than the array (not
+ * reachable within the other limits); MOE_ERR_HIP if the array's address cannot be found.
+ */
+int moe_permute_noalloc(const int32_t* topk_idx, int T, int E, int k, const void* x, int H,
+                        moe_dtype dtype, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                        int32_t* src_of, void* x_perm, int32_t* status, moe_stream_t stream);
+
+/*
  * moe_merge_weights -- make the merged buffer: write the slot map for the
  * expert set ids_host (strictly ascending; slot = position in ids_host) and
  * copy every expert of that set that the local pool holds into its slot
