@@ -64,6 +64,12 @@ def parse():
     p.add_argument("--workloads", default="r1_prefill_t8192_zipf,r1_prefill_t16384,r1_pipeline_6x4096",
                    help="other workloads timed in the same run and reported under 'workloads' "
                         "('none': only the headline)")
+    p.add_argument("--sdma-experts", type=int, default=0,
+                   help="pipelines: pull this many remote experts per layer as no-CU copies on a "
+                        "second copy stream, beside the rest (0: one copy stream)")
+    p.add_argument("--pipeline-chunks", type=int, default=1,
+                   help="pipelines: cut the main pull into this many expert-aligned chunks, each "
+                        "with its own ready event; the grouped GEMM runs per chunk as it lands")
     p.add_argument("--workload-steps", type=int, default=10)
     p.add_argument("--pipeline-steps", type=int, default=3)
     p.add_argument("--calibrate", action="store_true",
@@ -150,7 +156,9 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     from grouped_gemm_weights_amd.pipeline import MoEPipeline
 
     P = MoEPipeline(cfg, device=dev, copy_mode=copy_mode, stitched=args.merge == "stitched",
-                    fused_gather=args.gather == "fused")
+                    fused_gather=args.gather == "fused", sdma_experts=args.sdma_experts,
+                    chunks=args.pipeline_chunks)
+    split = P.split
     n = cfg.layers
     keys = ("c0", "c1", "wait0", "wait1", "d0", "m1", "g1")
     mk = lambda: {k: [B.moe_event_create(True) for _ in range(n)] for k in keys}
@@ -171,7 +179,9 @@ def bench_pipeline(args, cfg, dev, copy_mode):
             P_l.append(el(ev["c0"][l], ev["c1"][l]))
             stall.append(el(ev["wait0"][l], ev["wait1"][l]))
             comp_pipe.append(el(ev["d0"][l], ev["m1"][l]) - stall[-1])
-            gemm.append(el(ev["wait1"][l], ev["g1"][l]))
+            # split pull: the GEMM runs as expert ranges between waits, timed from the first
+            # wait to the last range's end (waits included: an upper bound)
+            gemm.append(el(ev["wait0" if split else "wait1"][l], ev["g1"][l]))
             if l > 0:
                 Lat.append(el(ev["m1"][l - 1], ev["m1"][l]))
     sev = mk()
@@ -188,7 +198,9 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     gc.collect()
     torch.cuda.empty_cache()
     mean = lambda v: float(np.mean(v))
-    H = 1.0 - sum(stall) / sum(P_l)
+    # with a split pull the compute stream runs expert ranges between its waits, so the time
+    # around the waits is not a stall: no hidden fraction then, the latency figures stand
+    H = None if split else 1.0 - sum(stall) / sum(P_l)
     eb = synth.expert_block_bytes(cfg)
     R = cfg.T * cfg.k
     gemm_ms = mean(gemm)
@@ -202,7 +214,9 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof.update({"traffic": None, "kernel": "moe_grouped_swiglu, pipelined layers (with the copy running)",
+    roof.update({"traffic": None,
+                 "kernel": "moe_grouped_swiglu, pipelined layers (with the copy running)" +
+                           (", expert ranges as the pull lands, waits included" if split else ""),
                  "avg_ms": round(gemm_ms, 4), "alg_bytes": alg_bytes, "alg_flop": alg_flop,
                  "TFLOPs": round(tflops, 1), "GBps": round(gbps, 1)})
     return {
@@ -215,15 +229,18 @@ def bench_pipeline(args, cfg, dev, copy_mode):
                    "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.k,
                    "local_experts": cfg.n_local, "copy_engine": args.copy_mode,
                    "copy_blocks": args.copy_blocks if args.copy_mode == "kernel" else None,
-                   "merge": args.merge, "gather": args.gather, "parallelism": "none (1 GPU)"},
+                   "merge": args.merge, "gather": args.gather, "sdma_experts": args.sdma_experts,
+                   "pull_chunks": args.pipeline_chunks, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "pipeline": {
             "prefetch_ms": round(mean(P_l), 3), "prefetch_alone_ms": round(mean(P_alone), 3),
             "copy_bytes": copy_bytes,
             "copy_GBps": round(copy_bytes / (mean(P_l) * 1e-3) / 1e9, 1),
-            "stall_ms": round(mean(stall), 3), "hidden_fraction": round(H, 4),
-            "compute_pipelined_ms": round(mean(comp_pipe), 3), "compute_alone_ms": round(mean(C_alone), 3),
-            "contention_slowdown": round(mean(comp_pipe) / mean(C_alone), 3),
+            "stall_ms": None if split else round(mean(stall), 3),
+            "hidden_fraction": None if H is None else round(H, 4),
+            "compute_pipelined_ms": None if split else round(mean(comp_pipe), 3),
+            "compute_alone_ms": round(mean(C_alone), 3),
+            "contention_slowdown": None if split else round(mean(comp_pipe) / mean(C_alone), 3),
             "layer_latency_ms": round(mean(Lat), 3),
             "layer_latency_ms_median": round(float(np.median(Lat)), 3),
             "layer_latency_ms_min": round(float(np.min(Lat)), 3),
@@ -410,7 +427,7 @@ def pipeline_summary(r):
            "steps": r["steps"], "roofline": r["roofline"]}
     out.update(r["pipeline"])
     out["config"] = {k: r["config"][k] for k in ("layers", "tokens", "merge", "gather",
-                                                  "copy_engine")}
+                                                  "copy_engine", "sdma_experts", "pull_chunks")}
     return out
 
 

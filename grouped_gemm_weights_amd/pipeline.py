@@ -38,9 +38,18 @@ class MoEPipeline:
     stream moves only the remote share; the halves' own blocks alternate between layers."""
 
     def __init__(self, cfg: synth.MoEConfig, device="cuda", copy_mode: int = B.MOE_COPY_KERNEL,
-                 stitched: bool = False, fused_gather: bool = False):
+                 stitched: bool = False, fused_gather: bool = False, sdma_experts: int = 0,
+                 chunks: int = 1):
+        """sdma_experts > 0 splits each layer's pull over two copy engines: the first
+        ``sdma_experts`` remote experts go as no-CU copies (MOE_COPY_SDMA) on a second copy
+        stream while the rest go through ``copy_mode`` on the first, in ``chunks`` runs of
+        whole experts.  Every part has its own ready event, and the MoE block runs the grouped
+        GEMM per expert range as each part lands (the local experts first)."""
         assert cfg.dtype == "bf16", "the pipeline runs the bf16 workloads"
+        assert 0 <= sdma_experts <= cfg.E - cfg.n_local and chunks >= 1
         self.cfg = cfg
+        self.sdma_experts = sdma_experts
+        self.chunks = chunks
         self.dev = torch.device(device)
         self.stitched = stitched
         self.L = MoELayer(cfg, device=self.dev, copy_mode=copy_mode, allocate_halves=not stitched,
@@ -63,6 +72,22 @@ class MoEPipeline:
             self.w_attn.append(synth.dense_weight_torch(cfg, l, self.dev))
         x0 = synth.activations(cfg, 0)
         self.x0 = torch.from_numpy(x0.view(np.int16)).view(torch.bfloat16).to(self.dev)
+        # the pull's parts: (expert range, stream) in the order the GEMM consumes them; the
+        # local experts [0, n_local) are ready once the merge has written the slot map
+        self.copy_stream2 = torch.cuda.Stream(device=self.dev) if sdma_experts else None
+        lo = cfg.n_local
+        parts = []
+        if sdma_experts:
+            parts.append((lo, lo + sdma_experts, "sdma"))
+            lo += sdma_experts
+        if lo < cfg.E:
+            bounds = np.linspace(lo, cfg.E, min(chunks, cfg.E - lo) + 1).round().astype(int)
+            parts += [(int(a), int(b), "main") for a, b in zip(bounds[:-1], bounds[1:])]
+        self.parts = parts
+        self.split = bool(sdma_experts) or chunks > 1
+        # ready events per half: [merge] + one per part
+        self.part_ready = [[B.moe_event_create(False) for _ in range(len(parts) + 1)]
+                           for _ in range(2)]
         self.x = torch.empty_like(self.x0)
         self.a = torch.empty_like(self.x0)
         self.all_ids = list(range(cfg.E))
@@ -95,6 +120,8 @@ class MoEPipeline:
     def fill(self, l: int, wait_free: bool = True, ev: Optional[Dict[str, list]] = None) -> None:
         """Copy stream: wait until half l % 2 is free, then merge layer l's local experts and
         prefetch its remote share into it; ``ev`` c0/c1 bracket the copies themselves."""
+        if self.split:
+            return self._fill_split(l, wait_free, ev)
         L, h = self.L, l % 2
         if wait_free:
             B.moe_stream_wait_event(L.copy_stream, L.free[h])
@@ -107,6 +134,38 @@ class MoEPipeline:
         if ev is not None:
             B.moe_event_record(ev["c1"][l], L.copy_stream)
 
+    def _fill_split(self, l: int, wait_free: bool, ev) -> None:
+        """The split pull: the merge and the main parts on copy stream 1 (``copy_mode``), the
+        SDMA part on copy stream 2 (no-CU copies), one ready event per part.  c1 is recorded
+        on stream 1 after stream 2's part has landed, so c0..c1 spans the whole pull."""
+        L, h, cfg = self.L, l % 2, self.cfg
+        s1, s2 = L.copy_stream, self.copy_stream2
+        ready = self.part_ready[h]
+        if wait_free:
+            B.moe_stream_wait_event(s1, L.free[h])
+            if s2 is not None:
+                B.moe_stream_wait_event(s2, L.free[h])
+        if ev is not None:
+            B.moe_event_record(ev["c0"][l], s1)
+            if s2 is not None:
+                B.moe_stream_wait_event(s2, ev["c0"][l])
+        B.moe_merge_weights(self.merge_pools[l], self.all_ids, self.wbufs[l], s1,
+                            wait_free=None, ready=ready[0], copy_mode=L.copy_mode)
+        rbase = self.remotes[l].data_ptr()
+        for i, (lo, hi, eng) in enumerate(self.parts):
+            sub = B.pool(rbase + (lo - cfg.n_local) * L.eb, L.eb, lo, hi - lo)
+            if eng == "sdma":
+                B.moe_prefetch_layer(sub, self.all_ids, self.wbufs[l], s2, ready=ready[i + 1],
+                                     copy_mode=B.MOE_COPY_SDMA)
+            else:
+                B.moe_prefetch_layer(sub, self.all_ids, self.wbufs[l], s1, ready=ready[i + 1],
+                                     copy_mode=L.copy_mode)
+        if s2 is not None:
+            B.moe_stream_wait_event(s1, ready[1])
+        B.moe_event_record(L.ready[h], s1)
+        if ev is not None:
+            B.moe_event_record(ev["c1"][l], s1)
+
     def dense(self, l: int) -> None:
         cfg = self.cfg
         B.moe_dense_gemm(self.x, self.w_attn[l], cfg.T, cfg.H, cfg.H, self.a, self.L.compute_stream)
@@ -118,10 +177,21 @@ class MoEPipeline:
         L.route_permute()
         if ev is not None:
             B.moe_event_record(ev["wait0"][l], cs)
-        B.moe_stream_wait_event(cs, L.ready[h])
-        if ev is not None:
-            B.moe_event_record(ev["wait1"][l], cs)
-        L.grouped(self.wbufs[l])
+        if self.split:
+            # per-part readiness: the local experts, then each part as it lands
+            ready = self.part_ready[h]
+            B.moe_stream_wait_event(cs, ready[0])
+            L.grouped(self.wbufs[l], 0, cfg.n_local)
+            for i, (lo, hi, _) in enumerate(self.parts):
+                B.moe_stream_wait_event(cs, ready[i + 1])
+                if ev is not None and i == len(self.parts) - 1:
+                    B.moe_event_record(ev["wait1"][l], cs)
+                L.grouped(self.wbufs[l], lo, hi)
+        else:
+            B.moe_stream_wait_event(cs, L.ready[h])
+            if ev is not None:
+                B.moe_event_record(ev["wait1"][l], cs)
+            L.grouped(self.wbufs[l])
         if ev is not None and "g1" in ev:
             B.moe_event_record(ev["g1"][l], cs)
         B.moe_combine(L.y_perm, L.row_of, L.topk_w, cfg.T, cfg.k, cfg.H, L.y, cs)
@@ -176,9 +246,16 @@ class MoEPipeline:
 
     def synchronize(self) -> None:
         self.L.synchronize()
+        if self.copy_stream2 is not None:
+            self.copy_stream2.synchronize()
 
     def close(self) -> None:
         """Release the stitched ranges and blocks (and the layer's events)."""
+        self.synchronize()
+        for lst in self.part_ready:
+            for e in lst:
+                B.moe_event_destroy(e)
+        self.part_ready = []
         self.L.close()
         for va, sizes in self._ranges:
             B.moe_vmm_unmap(va, sizes)

@@ -48,6 +48,60 @@ def test_r1_pipeline_6x4096(stitched):
         torch.cuda.empty_cache()
 
 
+def test_r1_pipeline_6x4096_dwdp3():
+    """The DWDP3 split (86 local experts, 170 pulled per layer), stitched merge, fused gather."""
+    from grouped_gemm_weights_amd.layer import block_to_numpy
+    from grouped_gemm_weights_amd.pipeline import MoEPipeline
+    cfg = synth.config("r1_pipeline_6x4096_dwdp3")
+    log(f"case {cfg.name}")
+    P = MoEPipeline(cfg, stitched=True, fused_gather=True)
+    try:
+        _check_pipeline(cfg, P, block_to_numpy, n_tokens=8)
+    finally:
+        P.close()
+        del P
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("sdma_experts,chunks", [(40, 3), (0, 4), (192, 1)],
+                         ids=["sdma40+3chunks", "4chunks", "all-sdma"])
+def test_r1_pipeline_6x4096_split_pull(sdma_experts, chunks):
+    """The pull split over two copy engines (no-CU copies on a second copy stream beside the
+    copy kernel) and cut into expert-aligned chunks with one ready event each; the grouped
+    GEMM runs per expert range as each part lands.  Same checks as the single-stream pull."""
+    from grouped_gemm_weights_amd.layer import block_to_numpy
+    from grouped_gemm_weights_amd.pipeline import MoEPipeline
+    cfg = synth.config("r1_pipeline_6x4096")
+    log(f"case {cfg.name} sdma_experts={sdma_experts} chunks={chunks}")
+    P = MoEPipeline(cfg, stitched=True, fused_gather=True, sdma_experts=sdma_experts,
+                    chunks=chunks)
+    try:
+        assert P.split
+        _check_pipeline(cfg, P, block_to_numpy, n_tokens=8)
+    finally:
+        P.close()
+        del P
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("sdma_experts,chunks", [(0, 1), (5, 2), (3, 5)])
+def test_small_pipeline_split_pull_full_layers(sdma_experts, chunks):
+    """A three-layer pipeline small enough to check every token of every layer: the split
+    pull (SDMA share + chunked main pull, per-part GEMM ranges) against the oracle."""
+    from grouped_gemm_weights_amd.layer import block_to_numpy
+    from grouped_gemm_weights_amd.pipeline import MoEPipeline
+    cfg = synth.MoEConfig("pipe_small_split", T=200, H=256, I=128, E=16, k=4, dtype="bf16",
+                          n_local=4, seed=71, layers=3, dense_standin=True)
+    log(f"case {cfg.name} sdma_experts={sdma_experts} chunks={chunks}")
+    P = MoEPipeline(cfg, stitched=False, sdma_experts=sdma_experts, chunks=chunks)
+    try:
+        _check_pipeline(cfg, P, block_to_numpy, n_tokens=cfg.T)
+    finally:
+        P.close()
+
+
 def test_r1_pipeline_4x16384():
     """Four layers at 16384 tokens each, stitched merge: the same checks as above."""
     from grouped_gemm_weights_amd.layer import block_to_numpy
