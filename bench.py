@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--gather", choices=["separate", "fused"], default="fused",
                    help="separate: moe_permute writes x_perm; fused: the grouped GEMM gathers its rows "
                         "from x on load (moe_grouped_swiglu_gathered)")
+    p.add_argument("--combine", choices=["separate", "epilogue"], default="separate",
+                   help="separate: grouped GEMM writes y_perm, moe_combine sums it; epilogue: the "
+                        "down GEMM adds its weighted rows into y (moe_grouped_swiglu_combine)")
     p.add_argument("--merge", choices=["copy", "stitched"], default="stitched",
                    help="copy the local experts into each merged half, or stitch the local "
                         "block into the half's virtual range so the merge copies nothing")
@@ -442,8 +445,9 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
     from grouped_gemm_weights_amd import synth
     from grouped_gemm_weights_amd.layer import MoELayer, block_to_numpy
 
+    comb = args.combine == "epilogue"
     L = MoELayer(cfg, device=dev, copy_mode=copy_mode, stitched=args.merge == "stitched",
-                 fused_gather=args.gather == "fused")
+                 fused_gather=args.gather == "fused", combine_in_epilogue=comb)
     local = synth.pool_torch(cfg, 0, 0, cfg.n_local, dev)
     remote = synth.pool_torch(cfg, 0, cfg.n_local, cfg.E - cfg.n_local, dev)
     L.set_pools(local, remote)
@@ -479,10 +483,14 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
         B.moe_stream_wait_event(cs, L.ready[h])
         if timed:
             B.moe_event_record(ev["gemm0"][i], cs)
-        L.grouped(L.wbufs[h])
+        if comb:
+            L.grouped_combine(L.wbufs[h])
+        else:
+            L.grouped(L.wbufs[h])
         if timed:
             B.moe_event_record(ev["gemm1"][i], cs)
-        B.moe_combine(L.y_perm, L.row_of, L.topk_w, cfg.T, cfg.k, cfg.H, L.y, cs)
+        if not comb:
+            B.moe_combine(L.y_perm, L.row_of, L.topk_w, cfg.T, cfg.k, cfg.H, L.y, cs)
         B.moe_event_record(L.free[h], cs)
         if timed:
             B.moe_event_record(ev["end"][i], cs)
@@ -543,7 +551,9 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
     n_active = int((counts > 0).sum())
     eb = synth.expert_block_bytes(cfg)
     R = cfg.T * cfg.k
-    alg_bytes = n_active * eb + R * cfg.H * 2 + R * cfg.H * 4       # weights read + x_perm + y_perm
+    # weights read + x_perm + y_perm; with the combine in the epilogue: + x rows read through
+    # src_of and y accumulated in place (T rows of H floats)
+    alg_bytes = n_active * eb + R * cfg.H * 2 + (cfg.T * cfg.H * 4 if comb else R * cfg.H * 4)
     alg_flop = 6.0 * cfg.H * cfg.I * R
     copy_bytes = (len(ids) - (cfg.n_local if args.merge == "stitched" else 0)) * eb
     gemm_gbps = alg_bytes / (gemm_ms * 1e-3) / 1e9
@@ -556,7 +566,9 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": None}
-    roof.update({"kernel": "moe_grouped_swiglu (tile plan + gate/up GEMM + down GEMM)",
+    roof.update({"kernel": "moe_grouped_swiglu_combine (tile plan + gate/up GEMM + down GEMM with "
+                           "the combine in its epilogue)" if comb else
+                           "moe_grouped_swiglu (tile plan + gate/up GEMM + down GEMM)",
                  "avg_ms": round(gemm_ms, 4), "alg_bytes": alg_bytes, "alg_flop": alg_flop})
     tr = traffic_from_profiles(cfg.name)
     if tr is not None:
@@ -581,7 +593,8 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
                    "experts": cfg.E, "top_k": cfg.k, "local_experts": cfg.n_local,
                    "remote_fetch": args.remote, "copy_engine": args.copy_mode,
                    "copy_blocks": args.copy_blocks if args.copy_mode == "kernel" else None,
-                   "merge": args.merge, "gather": args.gather, "fetch_chunks": nch, "parallelism": "none (1 GPU)"},
+                   "merge": args.merge, "gather": args.gather, "combine": args.combine,
+                   "fetch_chunks": nch, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "breakdown_ms": {"route_permute": round(rp_ms, 4), "merge_prefetch_copy": round(copy_ms, 4),
                          "grouped_swiglu": round(gemm_ms, 4), "combine": round(combine_ms, 4),

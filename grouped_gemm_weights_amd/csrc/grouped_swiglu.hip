@@ -42,6 +42,16 @@ struct Tile {
   int32_t slot;
 };
 
+// The combine folded into the down GEMM's epilogue: output row r of expert e belongs to
+// assignment a = src_of[r] (token a / k, slot a % k); its row is scaled by w[a] and added
+// into y[a / k] with a float atomic.  y = nullptr: plain stores into y_perm instead.
+struct Scatter {
+  const int32_t* src_of;
+  const float* w;
+  int k;
+  float* y;
+};
+
 constexpr int kMinBM = 16;        // smallest tile height: bounds the tile list
 constexpr int kWidePlanBM = 256;  // prefill tile height: tiles split into heavy and light lists
 
@@ -186,13 +196,16 @@ constexpr int kMGroup = 4;
 
 constexpr int kWideBM = 256, kWideBN = 256, kWideBK = 64, kWideLd = kWideBK + 8;
 
-// MI = 0: full tile; MI > 0: partial tile of at most MI * 32 rows
-template <bool DUAL, bool OUT_BF16, bool KFULL, int MI>
+// MI = 0: full tile; MI > 0: partial tile of at most MI * 32 rows.  COMB (down GEMM only):
+// the epilogue scatters w-scaled rows into y (Scatter) instead of storing them.
+template <bool DUAL, bool OUT_BF16, bool KFULL, int MI, bool COMB>
 __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16_t* __restrict__ A,
                                           int lda, const int32_t* __restrict__ a_index, int a_div,
                                           const uint16_t* __restrict__ B0,
                                           const uint16_t* __restrict__ B1, int N, int K,
-                                          void* __restrict__ out, int ldo, uint16_t* smem) {
+                                          void* __restrict__ out, int ldo, uint16_t* smem,
+                                          const Scatter& sc) {
+  static_assert(!COMB || (!DUAL && !OUT_BF16), "the combine runs in the f32 down GEMM");
   constexpr int BN = kWideBN, BK = kWideBK, NT = 256;
   constexpr int LDS_LD = kWideLd;
   constexpr int KC = BK / 8;            // 16-byte chunks per row per stage
@@ -417,6 +430,23 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
       }                                                                                \
     }                                                                                  \
   } while (0)
+  if constexpr (COMB) {
+    // y[a / k] += w[a] * row, one float atomic per element (the k rows of a token sit in k
+    // different experts' tiles, so no tile owns a token's sum)
+    _Pragma("unroll") for (int i = 0; i < MW; ++i)
+    _Pragma("unroll") for (int q = 0; q < 16; ++q) {
+      const int dr = i * 32 + (q >> 2) * 8 + (q & 3);
+      if (r0 + dr >= tile.rows) continue;
+      const int a = sc.src_of[tile.row0 + r0 + dr];
+      const float wa = sc.w[a];
+      float* const yrow = sc.y + static_cast<int64_t>(a / sc.k) * ldo + cw + lrow;
+      _Pragma("unroll") for (int j = 0; j < NO; ++j) {
+        if (cw + j * 32 + lrow >= N) continue;
+        unsafeAtomicAdd(yrow + j * 32, wa * acc[i][j][q]);
+      }
+    }
+    return;
+  }
   if (wm0 + MW * 32 <= tile.rows && cw + NO * 32 <= N)
     W_EPI(false);
   else
@@ -424,12 +454,13 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
 #undef W_EPI
 }
 
-template <bool DUAL, bool OUT_BF16, bool KFULL>
+template <bool DUAL, bool OUT_BF16, bool KFULL, bool COMB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_wide_kernel(
     const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ a_index, int a_div,
     const char* __restrict__ wbase, int64_t expert_bytes,
     int64_t b0_off, int64_t b1_off, int N, int K, const Tile* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, int dense_M, void* __restrict__ out, int ldo) {
+    const int32_t* __restrict__ n_tiles, int dense_M, void* __restrict__ out, int ldo,
+    Scatter sc) {
   constexpr int BM = kWideBM;
   constexpr int OUTN = DUAL ? kWideBN / 2 : kWideBN;
 
@@ -471,16 +502,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint16_t* B0 = reinterpret_cast<const uint16_t*>(wexp + b0_off);
   const uint16_t* B1 = reinterpret_cast<const uint16_t*>(wexp + b1_off);
   if (tile.rows > 192)
-    wide_tile<DUAL, OUT_BF16, KFULL, 0>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem);
+    wide_tile<DUAL, OUT_BF16, KFULL, 0, COMB>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem, sc);
   else if (tile.rows > 128)
-    wide_tile<DUAL, OUT_BF16, KFULL, 6>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem);
+    wide_tile<DUAL, OUT_BF16, KFULL, 6, COMB>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem, sc);
   else if (tile.rows > 64)
-    wide_tile<DUAL, OUT_BF16, KFULL, 4>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem);
+    wide_tile<DUAL, OUT_BF16, KFULL, 4, COMB>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem, sc);
   else
-    wide_tile<DUAL, OUT_BF16, KFULL, 2>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem);
+    wide_tile<DUAL, OUT_BF16, KFULL, 2, COMB>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem, sc);
 }
 
-template <bool DUAL, bool OUT_BF16>
+template <bool DUAL, bool OUT_BF16, bool COMB = false>
 struct GemmWide {
   static constexpr int BM = kWideBM;
   static constexpr size_t kLds =
@@ -491,9 +522,9 @@ struct GemmWide {
                     const char* wbase, int64_t expert_bytes,
                     int64_t b0_off, int64_t b1_off, int N, int K, const Tile* tiles,
                     const int32_t* n_tiles, int64_t grid_m, int dense_M, void* out, int ldo,
-                    hipStream_t s) {
-    auto kern = K % 64 == 0 ? gemm_wide_kernel<DUAL, OUT_BF16, true>
-                            : gemm_wide_kernel<DUAL, OUT_BF16, false>;
+                    hipStream_t s, Scatter sc = Scatter{nullptr, nullptr, 1, nullptr}) {
+    auto kern = K % 64 == 0 ? gemm_wide_kernel<DUAL, OUT_BF16, true, COMB>
+                            : gemm_wide_kernel<DUAL, OUT_BF16, false, COMB>;
     // the dynamic-LDS limit above 64 KB is set on every launch: it is a cheap host call
     // and, unlike a once-per-process flag, holds for every device and thread
     MOE_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -506,7 +537,7 @@ struct GemmWide {
     const int64_t blocks = ceil_div64(groups, kXcds) * kXcds * kMGroup * ceil_div(N, outn);
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), kLds, s, A, lda, a_index,
                        a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles, dense_M,
-                       out, ldo);
+                       out, ldo, sc);
     MOE_LAUNCH_CHECK("gemm_wide_kernel launch");
     return MOE_OK;
   }
@@ -526,12 +557,13 @@ struct GemmWide {
 
 //   NB  16-column MFMA blocks per wave (DUAL: NB / 2 gate + NB / 2 up blocks)
 //   KS  32-deep MFMA steps per register stage
-template <bool DUAL, bool KFULL, int NB, int KS>
+template <bool DUAL, bool KFULL, int NB, int KS, bool COMB>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ a_index, int a_div,
     const char* __restrict__ wbase, int64_t expert_bytes, int64_t b0_off, int64_t b1_off, int N,
     int K, const Tile* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
-    void* __restrict__ out, int ldo) {
+    void* __restrict__ out, int ldo, Scatter sc) {
+  static_assert(!COMB || !DUAL, "the combine runs in the down GEMM");
   constexpr int WCOLS = DUAL ? NB * 8 : NB * 16;
   constexpr int BCOLS = 4 * WCOLS;
   constexpr int SK = 32 * KS;  // K depth of one register stage
@@ -613,6 +645,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
           static_cast<uint16_t*>(out)[orow + n] =
               f32_to_bf16(silu_f32(acc[jj][q]) * acc[NB / 2 + jj][q]);
       }
+    } else if (COMB) {
+      // y[a / k] += w[a] * row (the combine folded into the epilogue)
+      const int a = sc.src_of[tile.row0 + r];
+      const float wa = sc.w[a];
+      float* const yrow = sc.y + static_cast<int64_t>(a / sc.k) * ldo;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = c0 + j * 16 + lr;
+        if (n < N) unsafeAtomicAdd(yrow + n, wa * acc[j][q]);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -623,24 +665,24 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   }
 }
 
-template <bool DUAL, int NB, int KS>
+template <bool DUAL, int NB, int KS, bool COMB = false>
 struct GemmStream {
   static constexpr int BM = 16;
   static constexpr int BCOLS = 4 * (DUAL ? NB * 8 : NB * 16);
   static int launch(const uint16_t* A, int lda, const int32_t* a_index, int a_div,
                     const char* wbase, int64_t expert_bytes, int64_t b0_off, int64_t b1_off, int N,
                     int K, const Tile* tiles, const int32_t* n_tiles, int64_t grid_tiles, void* out,
-                    int ldo, hipStream_t s) {
+                    int ldo, hipStream_t s, Scatter sc = Scatter{nullptr, nullptr, 1, nullptr}) {
     if (grid_tiles <= 0) return MOE_OK;
     dim3 grid(static_cast<unsigned>(grid_tiles), static_cast<unsigned>(ceil_div(N, BCOLS)));
     if (K % (32 * KS) == 0)
-      hipLaunchKernelGGL((gemm_stream_kernel<DUAL, true, NB, KS>), grid, dim3(256), 0, s, A, lda,
-                         a_index, a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles,
-                         out, ldo);
+      hipLaunchKernelGGL((gemm_stream_kernel<DUAL, true, NB, KS, COMB>), grid, dim3(256), 0, s, A,
+                         lda, a_index, a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles,
+                         n_tiles, out, ldo, sc);
     else
-      hipLaunchKernelGGL((gemm_stream_kernel<DUAL, false, NB, KS>), grid, dim3(256), 0, s, A, lda,
-                         a_index, a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles, n_tiles,
-                         out, ldo);
+      hipLaunchKernelGGL((gemm_stream_kernel<DUAL, false, NB, KS, COMB>), grid, dim3(256), 0, s, A,
+                         lda, a_index, a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles,
+                         n_tiles, out, ldo, sc);
     MOE_LAUNCH_CHECK("gemm_stream_kernel launch");
     return MOE_OK;
   }
@@ -649,10 +691,12 @@ struct GemmStream {
 // decode shapes: gate/up with 2 + 2 blocks per wave, down with 4, 128-deep stages
 using Gemm1Stream = GemmStream<true, 4, 4>;
 using Gemm2Stream = GemmStream<false, 4, 4>;
+using Gemm2StreamComb = GemmStream<false, 4, 4, true>;
 
 // prefill shapes: 256-row tiles
 using Gemm1Prefill = GemmWide<true, false>;
 using Gemm2Prefill = GemmWide<false, false>;
+using Gemm2PrefillComb = GemmWide<false, false, true>;
 using DenseBf16 = GemmWide<false, true>;
 
 // ---------------------------------------------------------------------------
@@ -742,10 +786,18 @@ namespace {
 
 // The grouped SwiGLU over experts [e_begin, e_end).  A row r of the gate/up GEMM is row r of
 // x_perm, or, when a_index is given, row a_index[r] / a_div of x (the gather done on load).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += step)
+    p[i] = 0.f;
+}
+
+// sc (optional): the combine folded into the down GEMM (y_perm is then not written).
 int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
                         const int32_t* offsets, int R, int E, int H, int I, moe_dtype dtype,
                         const moe_wbuf* w, int e_begin, int e_end, void* ws, size_t ws_bytes,
-                        float* y_perm, int32_t* status, moe_stream_t stream) {
+                        float* y_perm, int32_t* status, moe_stream_t stream,
+                        const Scatter* sc = nullptr) {
   if (e_begin < 0 || e_end > E || e_begin > e_end)
     return fail(MOE_ERR_ARG, "moe_grouped_swiglu: expert range [%d, %d) outside [0, %d)", e_begin,
                 e_end, E);
@@ -768,7 +820,7 @@ int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
   if (!ws || ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_grouped_swiglu: workspace %zu < %zu bytes", ws_bytes, L.total);
   if (R == 0) return MOE_OK;
-  if (!x_perm || !y_perm) return fail(MOE_ERR_ARG, "moe_grouped_swiglu: null pointer");
+  if (!x_perm || (!y_perm && !sc)) return fail(MOE_ERR_ARG, "moe_grouped_swiglu: null pointer");
 
   hipStream_t s = as_stream(stream);
   char* wsb = static_cast<char*>(ws);
@@ -798,6 +850,15 @@ int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
                 "or more", static_cast<long long>(R) / a_div + 1, H);
   const int BM = decode ? 16 : Gemm1Prefill::BM;
   const int64_t grid_tiles = ceil_div64(R, BM) + std::min(E, R);
+  if (sc) {
+    // y is accumulated into: clear it on the stream first (a kernel, so the call can be
+    // captured into a graph)
+    const int64_t n = static_cast<int64_t>(R / sc->k) * H;
+    hipLaunchKernelGGL(zero_f32_kernel,
+                       dim3(static_cast<unsigned>(std::min<int64_t>(ceil_div64(n, 256), 65536))),
+                       dim3(256), 0, s, sc->y, n);
+    MOE_LAUNCH_CHECK("moe_grouped_swiglu_combine: clear y");
+  }
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(MOE_MAX_E), 0, s, offsets, E, e_begin, e_end, BM,
                      w->slot_of, w->n_slots, tiles, n_tiles, status);
   MOE_LAUNCH_CHECK("moe_grouped_swiglu: plan");
@@ -810,14 +871,22 @@ int grouped_swiglu_impl(const void* x_perm, const int32_t* a_index, int a_div,
     rc = Gemm1Stream::launch(xp, H, a_index, a_div, wbase, eb, 0, HI2, I, H, tiles, n_tiles,
                                   grid_tiles, h, I, s);
     if (rc) return rc;
-    rc = Gemm2Stream::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
-                                   grid_tiles, y_perm, H, s);
+    if (sc)
+      rc = Gemm2StreamComb::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
+                                   grid_tiles, nullptr, H, s, *sc);
+    else
+      rc = Gemm2Stream::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
+                               grid_tiles, y_perm, H, s);
   } else {
     rc = Gemm1Prefill::launch(xp, H, a_index, a_div, wbase, eb, 0, HI2, I, H, tiles, n_tiles,
                               grid_tiles, 0, h, I, s);
     if (rc) return rc;
-    rc = Gemm2Prefill::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
-                              grid_tiles, 0, y_perm, H, s);
+    if (sc)
+      rc = Gemm2PrefillComb::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
+                                    grid_tiles, 0, nullptr, H, s, *sc);
+    else
+      rc = Gemm2Prefill::launch(hp, I, nullptr, 1, wbase, eb, 2 * HI2, 0, H, I, tiles, n_tiles,
+                                grid_tiles, 0, y_perm, H, s);
   }
   return rc;
 }
@@ -845,6 +914,26 @@ extern "C" int moe_grouped_swiglu_gathered(const void* x, const int32_t* src_of,
                              ws_bytes, y_perm, status, stream);
 }
 
+
+extern "C" int moe_grouped_swiglu_combine(const void* x, const int32_t* src_of,
+                                          const float* topk_w, int T, int k,
+                                          const int32_t* offsets, int E, int H, int I,
+                                          moe_dtype dtype, const moe_wbuf* w, void* ws,
+                                          size_t ws_bytes, float* y, int32_t* status,
+                                          moe_stream_t stream) {
+  using namespace moe;
+  if (T < 0 || k < 1) return fail(MOE_ERR_ARG, "moe_grouped_swiglu_combine: T=%d k=%d", T, k);
+  if (dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_swiglu_combine: bf16 weights only");
+  const int64_t R64 = static_cast<int64_t>(T) * k;
+  if (R64 > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_swiglu_combine: T*k too large");
+  const int R = static_cast<int>(R64);
+  if (T > 0 && (!y || !src_of || !topk_w))
+    return fail(MOE_ERR_ARG, "moe_grouped_swiglu_combine: null pointer");
+  const Scatter sc{src_of, topk_w, k, y};
+  return grouped_swiglu_impl(x, src_of, k, offsets, R, E, H, I, dtype, w, 0, E, ws, ws_bytes,
+                             nullptr, status, stream, &sc);
+}
 
 extern "C" int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int R, int E, int H,
                                   int I, moe_dtype dtype, const moe_wbuf* w, void* ws,

@@ -45,13 +45,18 @@ class MoELayer:
     def __init__(self, cfg: MoEConfig, device="cuda", n_slots: Optional[int] = None,
                  n_halves: int = 2, compute_stream=None, copy_stream=None,
                  copy_mode: int = B.MOE_COPY_KERNEL, stitched: bool = False,
-                 allocate_halves: bool = True, fused_gather: bool = False):
+                 allocate_halves: bool = True, fused_gather: bool = False,
+                 combine_in_epilogue: bool = False):
         """stitched: each half is one virtual range over [the local-expert block | the half's own
         block], so merging the local experts copies nothing (page stitching, moe_vmm_*).
         allocate_halves=False leaves the halves to the caller (the pipeline builds per-layer ranges).
-        fused_gather: the grouped GEMM reads its rows from x through src_of, and x_perm is not built."""
+        fused_gather: the grouped GEMM reads its rows from x through src_of, and x_perm is not built.
+        combine_in_epilogue: the down GEMM adds its w-scaled rows straight into y
+        (moe_grouped_swiglu_combine; implies fused_gather), and y_perm is not written."""
         self.cfg = cfg
         self.stitched = stitched
+        self.combine_in_epilogue = combine_in_epilogue
+        fused_gather = fused_gather or combine_in_epilogue
         self.fused_gather = fused_gather
         self.dev = torch.device(device)
         self.copy_mode = copy_mode
@@ -73,7 +78,7 @@ class MoELayer:
         self.src_of = torch.empty((R,), **i32)
         # with the gather fused into the GEMM's loads, x_perm is never written
         self.x_perm = torch.empty((1 if fused_gather else R, H), dtype=tdt, device=d)
-        self.y_perm = torch.empty((R, H), dtype=torch.float32, device=d)
+        self.y_perm = torch.empty((1 if combine_in_epilogue else R, H), dtype=torch.float32, device=d)
         self.y = torch.empty((T, H), dtype=torch.float32, device=d)
         self.status = torch.zeros((1,), **i32)
         self.ws_perm_bytes = B.moe_permute_workspace_size(T, E, k)
@@ -178,6 +183,25 @@ class MoELayer:
                                        self.dt, wbuf, e_begin, e_end, self.ws_gemm,
                                        self.ws_gemm_bytes, self.y_perm, self.status, cs)
 
+    def grouped_combine(self, wbuf, stream=None) -> None:
+        """Grouped SwiGLU GEMM with the gather on load and the combine in the down GEMM's
+        epilogue: writes y directly (every expert of ``wbuf``)."""
+        cfg = self.cfg
+        cs = self.compute_stream if stream is None else stream
+        B.moe_grouped_swiglu_combine(self.x, self.src_of, self.topk_w, cfg.T, cfg.k, self.offsets,
+                                     cfg.E, cfg.H, cfg.I, self.dt, wbuf, self.ws_gemm,
+                                     self.ws_gemm_bytes, self.y, self.status, cs)
+
+    def expert_output(self, wbuf) -> None:
+        """y from the merged buffer: the grouped GEMM then the combine, or both in one call."""
+        cfg = self.cfg
+        if self.combine_in_epilogue:
+            self.grouped_combine(wbuf)
+        else:
+            self.grouped(wbuf)
+            B.moe_combine(self.y_perm, self.row_of, self.topk_w, cfg.T, cfg.k, cfg.H, self.y,
+                          self.compute_stream)
+
     def routed_ids(self) -> Sequence[int]:
         """Read counts back (one small copy and a sync) and return the expert set of the buffer:
         every local expert plus the remote experts that received tokens, ascending."""
@@ -206,10 +230,9 @@ class MoELayer:
 
     def expert_compute(self, half: int) -> None:
         """Compute stream: wait for the half, grouped SwiGLU GEMM, combine, release the half."""
-        cfg, cs = self.cfg, self.compute_stream
+        cs = self.compute_stream
         B.moe_stream_wait_event(cs, self.ready[half])
-        self.grouped(self.wbufs[half])
-        B.moe_combine(self.y_perm, self.row_of, self.topk_w, cfg.T, cfg.k, cfg.H, self.y, cs)
+        self.expert_output(self.wbufs[half])
         B.moe_event_record(self.free[half], cs)
 
     def forward(self, half: int = 0, remote: str = "routed", chunks: int = 0, ev=None) -> None:
@@ -219,7 +242,7 @@ class MoELayer:
         GEMM runs per chunk as its weights land (the local experts first, while the copies run)."""
         self.route_permute()
         ids = self.routed_ids() if remote == "routed" else list(range(self.cfg.E))
-        if chunks <= 0:
+        if chunks <= 0 or self.combine_in_epilogue:
             self.fill_half(half, ids)
             self.expert_compute(half)
         else:

@@ -286,6 +286,24 @@ int moe_grouped_swiglu_gathered(const void* x, const int32_t* src_of, int k, con
                                 int32_t* status, moe_stream_t stream);
 
 /*
+ * moe_grouped_swiglu_combine -- the grouped SwiGLU GEMM with the row gather folded into its
+ * operand loads (as moe_grouped_swiglu_gathered) and the combine folded into the down
+ * GEMM's epilogue: each output row of assignment a = src_of[r] is scaled by topk_w[a] and
+ * added into y[a / k] with a float atomic, so neither x_perm nor y_perm is written (the
+ * groupedGEMM of the DWDP explainer's contiguous-buffer panel, producing the layer output).
+ * y is cleared on the stream first.  The k terms of a token are added in whatever order
+ * the tiles finish, so y agrees with moe_combine's fixed-order sum to rounding, not bit for
+ * bit, and can differ in its last bits from run to run.  All experts of the buffer.
+ *   x device [T][H] bf16; src_of device i32[T*k]; topk_w device f32[T][k]; y device f32[T][H]
+ *   offsets, w, ws (moe_grouped_swiglu_workspace_size(T*k, ...)), status: as moe_grouped_swiglu.
+ * Errors: as moe_grouped_swiglu_gathered; MOE_ERR_UNSUPPORTED for MOE_F32.
+ */
+int moe_grouped_swiglu_combine(const void* x, const int32_t* src_of, const float* topk_w, int T,
+                               int k, const int32_t* offsets, int E, int H, int I, moe_dtype dtype,
+                               const moe_wbuf* w, void* ws, size_t ws_bytes, float* y,
+                               int32_t* status, moe_stream_t stream);
+
+/*
  * moe_combine -- the weighted un-permute:
  *   y[t] = sum_{j=0..k-1} topk_w[t][j] * y_perm[row_of[t*k + j]], summed in j order, f32.
  * The pages give no combine rule of their own (like routing, the mixture only appears

@@ -250,3 +250,20 @@ def tokens_layer(weights_of, x_rows, logits_rows, k, H, I, round_h=True, workers
     for e, a in by_e.items():
         yp[a] = ffn[e]
     return O.combine(yp, np.arange(n * k), w, k)
+
+
+def check_y_tokens(cfg, L, tokens, layer: int = 0, workers=8):
+    """Routing and permutation bit-exact on all tokens; y of the given tokens against the
+    oracle's per-token layer (for paths that write no y_perm)."""
+    out = L.outputs()
+    assert out["status"] == 0, f"device status {out['status']}"
+    x = synth.activations(cfg, layer)
+    logits = synth.logits(cfg, layer)
+    check_routing(cfg, out, logits)
+    tokens = [int(t) for t in tokens]
+    y_ref = tokens_layer(weights_fn(L), np.asarray(x)[tokens], logits[tokens], cfg.k, cfg.H, cfg.I,
+                         round_h=cfg.dtype == "bf16", workers=workers)
+    e_y = rel_err(out["y"][tokens], y_ref)
+    log(f"{cfg.name}: y on {len(tokens)} tokens: err/rms {e_y:.3e} (tol {TOL[cfg.dtype]})")
+    assert e_y <= TOL[cfg.dtype]
+    return out

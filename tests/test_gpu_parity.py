@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from moe_cases import (O, TOL, build_layer, check_full, check_routing, check_rows, check_sampled,
-                       log, rel_err, synth, tile_boundary_rows, weights_fn)
+                       check_y_tokens, log, rel_err, synth, tile_boundary_rows, weights_fn)
 
 pytestmark = pytest.mark.gpu
 
@@ -512,3 +512,62 @@ def test_r1_prefill_t16384():
     log(f"case {cfg.name}")
     L = _run(build_layer(cfg), remote="all")
     check_rows(cfg, L, tile_boundary_rows, _sample(cfg.T, 64, 3))
+
+
+# ----------------------------------------------------------------------------
+# the combine folded into the down GEMM's epilogue (moe_grouped_swiglu_combine)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H,I,E,k,n_local", [
+    (50, 136, 72, 37, 3, 9),       # decode tiles, K and N tails
+    (300, 128, 64, 8, 2, 2),       # prefill tiles, ragged tail
+    (700, 256, 192, 12, 2, 3),     # full 256-row tiles and a partial column block
+    (12, 1024, 200, 40, 6, 10),    # decode tiles, K = 1024
+    (64, 256, 512, 8, 1, 4),       # k = 1
+])
+def test_combine_in_epilogue_small(T, H, I, E, k, n_local):
+    """Every token's y against the oracle, and against the two-call path (grouped GEMM then
+    moe_combine) to fp32 rounding: the atomics add a token's k rows in no fixed order."""
+    cfg = synth.MoEConfig(f"bf16_comb_T{T}_E{E}_k{k}", T=T, H=H, I=I, E=E, k=k, dtype="bf16",
+                          n_local=n_local, seed=3000 + T + E)
+    log(f"case {cfg.name}")
+    L = build_layer(cfg, combine_in_epilogue=True)
+    L.forward(half=0)
+    out = L.outputs()
+    assert out["status"] == 0
+    check_routing(cfg, out, synth.logits(cfg))
+    ref = O.moe_layer(synth.activations(cfg), synth.logits(cfg), cfg.k, weights_fn(L), cfg.H,
+                      cfg.I, True)
+    e_y = rel_err(out["y"], ref["y"])
+    L2 = build_layer(cfg, fused_gather=True)
+    L2.forward(half=0)
+    y2 = L2.outputs()["y"]
+    e_2 = rel_err(out["y"], y2)
+    log(f"{cfg.name}: y err/rms {e_y:.3e}; against the two-call path {e_2:.3e}")
+    assert e_y <= TOL["bf16"]
+    assert e_2 <= 1e-5
+    if k == 1:
+        # one term per token: the atomic adds w = 1.0 times the row to zero, exactly
+        np.testing.assert_array_equal(out["y"], y2)
+
+
+def test_combine_in_epilogue_r1_decode_t64():
+    cfg = synth.config("r1_decode_t64")
+    log(f"case {cfg.name} combine in epilogue")
+    L = build_layer(cfg, stitched=True, combine_in_epilogue=True)
+    try:
+        _run(L)
+        check_y_tokens(cfg, L, range(cfg.T))
+    finally:
+        L.close()
+
+
+def test_combine_in_epilogue_r1_prefill_t16384():
+    cfg = synth.config("r1_prefill_t16384")
+    log(f"case {cfg.name} combine in epilogue")
+    L = build_layer(cfg, stitched=True, combine_in_epilogue=True)
+    try:
+        L.forward(half=0, remote="all")
+        check_y_tokens(cfg, L, _sample(cfg.T, 64, 17))
+    finally:
+        L.close()
