@@ -64,9 +64,15 @@ def parse():
     p.add_argument("--cpu-single-thread-tokens", type=int, default=8,
                    help="tokens of the layer also run through the CPU bulk path with one BLAS "
                         "thread (0: skip)")
-    p.add_argument("--workloads", default="r1_prefill_t8192_zipf,r1_prefill_t16384,r1_pipeline_6x4096",
+    p.add_argument("--workloads",
+                   default="r1_prefill_t8192_zipf,r1_prefill_t16384,r1_pipeline_6x4096,"
+                           "r1_decode_t64_host_pool",
                    help="other workloads timed in the same run and reported under 'workloads' "
-                        "('none': only the headline)")
+                        "('none': only the headline); a name ending in _host_pool is that "
+                        "workload with its remote pool in pinned host memory")
+    p.add_argument("--remote-pool", choices=["device", "host"], default="device",
+                   help="where the remote experts live: a device pool, or pinned host memory "
+                        "(pulled over PCIe by the runtime copy)")
     p.add_argument("--sdma-experts", type=int, default=0,
                    help="pipelines: pull this many remote experts per layer as no-CU copies on a "
                         "second copy stream, beside the rest (0: one copy stream)")
@@ -389,16 +395,22 @@ def main():
         return
     host_blocks = {}
     result = bench_layer(args, cfg, dev, copy_mode, args.steps, args.warmup, args.alt_steps,
-                         headline=True, host_blocks=host_blocks)
+                         headline=True, host_blocks=host_blocks,
+                         remote_on_host=args.remote_pool == "host")
     # the other R1 workloads in the same run, each timed as above (default options), so the
     # prefill MFMA fractions and the pipeline's overlap figures sit beside the headline
     names = [w for w in args.workloads.split(",") if w and w != "none"]
     if names:
         wl = {}
         for name in names:
-            c = synth.config(name)
+            host_pool = name.endswith("_host_pool")
+            c = synth.config(name[: -len("_host_pool")] if host_pool else name)
             t0 = time.perf_counter()
-            if c.layers == 1:
+            if host_pool:
+                # the offload variant: every pull crosses PCIe, so a few steps suffice
+                r = bench_layer(args, c, dev, copy_mode, 3, 1, 0, remote_on_host=True)
+                wl[name] = layer_summary(r)
+            elif c.layers == 1:
                 r = bench_layer(args, c, dev, copy_mode, args.workload_steps, 2, 0)
                 wl[name] = layer_summary(r)
             else:
@@ -421,7 +433,7 @@ def layer_summary(r):
             "active_experts", "gemm_TFLOPs", "hbm_frac", "mfma_frac")
     out = {k: r[k] for k in keep if k in r}
     out["config"] = {k: r["config"][k] for k in ("tokens", "remote_fetch", "merge", "gather",
-                                                  "copy_engine")}
+                                                  "copy_engine", "combine")}
     return out
 
 
@@ -435,7 +447,7 @@ def pipeline_summary(r):
 
 
 def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=False,
-                host_blocks=None):
+                host_blocks=None, remote_on_host=False):
     """One MoE layer step timed over ``steps`` steps; returns its record.  With ``headline``
     the record also carries the input digests and the layer output (for the CPU comparison),
     and host copies of the routed experts' blocks are left in ``host_blocks``."""
@@ -450,6 +462,12 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
                  fused_gather=args.gather == "fused", combine_in_epilogue=comb)
     local = synth.pool_torch(cfg, 0, 0, cfg.n_local, dev)
     remote = synth.pool_torch(cfg, 0, cfg.n_local, cfg.E - cfg.n_local, dev)
+    if remote_on_host:
+        host = torch.empty(remote.shape, dtype=remote.dtype, pin_memory=True)
+        host.copy_(remote)
+        del remote
+        torch.cuda.empty_cache()
+        remote = host
     L.set_pools(local, remote)
     L.set_inputs(synth.activations(cfg), synth.logits(cfg))
     cs, ps = L.compute_stream, L.copy_stream
@@ -556,6 +574,7 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
     alg_bytes = n_active * eb + R * cfg.H * 2 + (cfg.T * cfg.H * 4 if comb else R * cfg.H * 4)
     alg_flop = 6.0 * cfg.H * cfg.I * R
     copy_bytes = (len(ids) - (cfg.n_local if args.merge == "stitched" else 0)) * eb
+    remote_pulled = sum(1 for e in ids if e >= cfg.n_local) * eb
     gemm_gbps = alg_bytes / (gemm_ms * 1e-3) / 1e9
     gemm_tflops = alg_flop / (gemm_ms * 1e-3) / 1e12
     ai = alg_flop / alg_bytes
@@ -600,7 +619,9 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
                          "grouped_swiglu": round(gemm_ms, 4), "combine": round(combine_ms, 4),
                          "layer_events": round(layer_ms, 4)},
         "timing": timing,
-        "copy": {"bytes": copy_bytes, "experts": len(ids), "GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1)},
+        "copy": {"bytes": copy_bytes, "experts": len(ids), "GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+                 "remote_pool": "pinned host" if remote_on_host else "device",
+                 "remote_bytes": remote_pulled},
         "active_experts": n_active,
         "gemm_TFLOPs": round(gemm_tflops, 2),
         "hbm_frac": round(gemm_gbps / HBM_PEAK_GBPS, 4),

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_STATUS = -5
 MOE_STATUS_NONFINITE_LOGIT, MOE_STATUS_EXPERT_ABSENT, MOE_STATUS_BAD_EXPERT_ID = 1, 2, 4
 MOE_COPY_SDMA, MOE_COPY_ANY, MOE_COPY_KERNEL = 0, 1, 2
 

@@ -76,7 +76,7 @@ extern "C" int moe_combine(const float* y_perm, const int32_t* row_of, const flo
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(256), 0, s, y_perm, row_of, topk_w, T, k, H, y);
   MOE_LAUNCH_CHECK("moe_combine: launch");
-  return MOE_OK;
+  return debug_check(MOE_OK, "moe_combine", s, nullptr);
 }
 
 extern "C" int moe_residual_add(const void* x, const float* y, int64_t n, void* out,
@@ -90,5 +90,5 @@ extern "C" int moe_residual_add(const void* x, const float* y, int64_t n, void* 
   hipLaunchKernelGGL(residual_kernel, dim3(blocks), dim3(256), 0, as_stream(stream),
                      static_cast<const uint16_t*>(x), y, n, static_cast<uint16_t*>(out));
   MOE_LAUNCH_CHECK("moe_residual_add: launch");
-  return MOE_OK;
+  return debug_check(MOE_OK, "moe_residual_add", as_stream(stream), nullptr);
 }

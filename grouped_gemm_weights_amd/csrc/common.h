@@ -28,6 +28,11 @@ inline int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+// Debug mode (MOE_DEBUG_SYNC set to anything but "" or "0"): every call that enqueued work
+// synchronises its stream before it returns; a failed kernel becomes MOE_ERR_HIP and a set
+// status bit MOE_ERR_STATUS, each with a description.  rc != MOE_OK passes through.
+int debug_check(int rc, const char* who, hipStream_t s, const int32_t* status);
+
 inline int hip_fail(hipError_t e, const char* what) {
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }

@@ -898,8 +898,9 @@ extern "C" int moe_grouped_swiglu_range(const void* x_perm, const int32_t* offse
                                         int H, int I, moe_dtype dtype, const moe_wbuf* w,
                                         int e_begin, int e_end, void* ws, size_t ws_bytes,
                                         float* y_perm, int32_t* status, moe_stream_t stream) {
-  return moe::grouped_swiglu_impl(x_perm, nullptr, 1, offsets, R, E, H, I, dtype, w, e_begin, e_end,
-                                  ws, ws_bytes, y_perm, status, stream);
+  const int rc = moe::grouped_swiglu_impl(x_perm, nullptr, 1, offsets, R, E, H, I, dtype, w,
+                                          e_begin, e_end, ws, ws_bytes, y_perm, status, stream);
+  return moe::debug_check(rc, "moe_grouped_swiglu_range", moe::as_stream(stream), status);
 }
 
 extern "C" int moe_grouped_swiglu_gathered(const void* x, const int32_t* src_of, int k,
@@ -910,8 +911,9 @@ extern "C" int moe_grouped_swiglu_gathered(const void* x, const int32_t* src_of,
   using namespace moe;
   if (k < 1) return fail(MOE_ERR_ARG, "moe_grouped_swiglu_gathered: k=%d", k);
   if (R > 0 && !src_of) return fail(MOE_ERR_ARG, "moe_grouped_swiglu_gathered: null src_of");
-  return grouped_swiglu_impl(x, src_of, k, offsets, R, E, H, I, dtype, w, e_begin, e_end, ws,
-                             ws_bytes, y_perm, status, stream);
+  const int rc = grouped_swiglu_impl(x, src_of, k, offsets, R, E, H, I, dtype, w, e_begin, e_end,
+                                     ws, ws_bytes, y_perm, status, stream);
+  return debug_check(rc, "moe_grouped_swiglu_gathered", as_stream(stream), status);
 }
 
 
@@ -931,8 +933,9 @@ extern "C" int moe_grouped_swiglu_combine(const void* x, const int32_t* src_of,
   if (T > 0 && (!y || !src_of || !topk_w))
     return fail(MOE_ERR_ARG, "moe_grouped_swiglu_combine: null pointer");
   const Scatter sc{src_of, topk_w, k, y};
-  return grouped_swiglu_impl(x, src_of, k, offsets, R, E, H, I, dtype, w, 0, E, ws, ws_bytes,
-                             nullptr, status, stream, &sc);
+  const int rc = grouped_swiglu_impl(x, src_of, k, offsets, R, E, H, I, dtype, w, 0, E, ws,
+                                     ws_bytes, nullptr, status, stream, &sc);
+  return debug_check(rc, "moe_grouped_swiglu_combine", as_stream(stream), status);
 }
 
 extern "C" int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int R, int E, int H,
@@ -954,7 +957,8 @@ extern "C" int moe_dense_gemm(const void* x, const void* w, int M, int N, int K,
                 static_cast<long long>(N) * K);
   if (M == 0) return MOE_OK;
   if (!x || !w || !out) return fail(MOE_ERR_ARG, "moe_dense_gemm: null pointer");
-  return DenseBf16::launch(static_cast<const uint16_t*>(x), K, nullptr, 1, static_cast<const char*>(w), 0, 0, 0,
-                           N, K, nullptr, nullptr, ceil_div(M, DenseBf16::BM), M, out, N,
-                           as_stream(stream));
+  const int rc = DenseBf16::launch(static_cast<const uint16_t*>(x), K, nullptr, 1,
+                                   static_cast<const char*>(w), 0, 0, 0, N, K, nullptr, nullptr,
+                                   ceil_div(M, DenseBf16::BM), M, out, N, as_stream(stream));
+  return debug_check(rc, "moe_dense_gemm", as_stream(stream), nullptr);
 }

@@ -317,8 +317,9 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int E, int k, const v
                            moe_dtype dtype, int32_t* counts, int32_t* offsets, int32_t* row_of,
                            int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes,
                            int32_t* status, moe_stream_t stream) {
-  return moe::permute_impl("moe_permute", topk_idx, T, E, k, x, H, dtype, counts, offsets, row_of,
-                           src_of, x_perm, ws, ws_bytes, status, stream);
+  const int rc = moe::permute_impl("moe_permute", topk_idx, T, E, k, x, H, dtype, counts, offsets,
+                                   row_of, src_of, x_perm, ws, ws_bytes, status, stream);
+  return moe::debug_check(rc, "moe_permute", moe::as_stream(stream), status);
 }
 
 extern "C" int moe_permute_noalloc(const int32_t* topk_idx, int T, int E, int k, const void* x,
@@ -338,6 +339,8 @@ extern "C" int moe_permute_noalloc(const int32_t* topk_idx, int T, int E, int k,
   void* scratch = nullptr;
   const int rc = scratch_on_current_device(&scratch);
   if (rc) return rc;
-  return permute_impl("moe_permute_noalloc", topk_idx, T, E, k, x, H, dtype, counts, offsets,
-                      row_of, src_of, x_perm, scratch, kPermuteScratchBytes, status, stream);
+  const int rc2 = permute_impl("moe_permute_noalloc", topk_idx, T, E, k, x, H, dtype, counts,
+                               offsets, row_of, src_of, x_perm, scratch, kPermuteScratchBytes,
+                               status, stream);
+  return debug_check(rc2, "moe_permute_noalloc", as_stream(stream), status);
 }

@@ -111,5 +111,5 @@ extern "C" int moe_route(const float* logits, int T, int E, int k, int32_t* topk
   else if (E <= 512) launch_route<8>(logits, T, E, k, topk_idx, topk_w, status, s);
   else launch_route<16>(logits, T, E, k, topk_idx, topk_w, status, s);
   MOE_LAUNCH_CHECK("moe_route: launch");
-  return MOE_OK;
+  return debug_check(MOE_OK, "moe_route", s, status);
 }

@@ -31,6 +31,28 @@ std::string& last_error() {
   return s;
 }
 
+int debug_check(int rc, const char* who, hipStream_t s, const int32_t* status) {
+  if (rc != MOE_OK) return rc;
+  const char* v = std::getenv("MOE_DEBUG_SYNC");
+  if (!v || !*v || std::strcmp(v, "0") == 0) return rc;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(MOE_ERR_HIP, "%s (debug sync): %s", who, hipGetErrorString(e));
+  if (status) {
+    int32_t bits = 0;
+    e = hipMemcpy(&bits, status, sizeof(bits), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+      return fail(MOE_ERR_HIP, "%s (debug sync, status read): %s", who, hipGetErrorString(e));
+    if (bits)
+      return fail(MOE_ERR_STATUS, "%s (debug sync): device status 0x%x:%s%s%s", who, bits,
+                  (bits & MOE_STATUS_NONFINITE_LOGIT) ? " non-finite logit" : "",
+                  (bits & MOE_STATUS_EXPERT_ABSENT) ? " expert absent from the merged buffer" : "",
+                  (bits & MOE_STATUS_BAD_EXPERT_ID) ? " expert id out of range" : "");
+  }
+  return MOE_OK;
+}
+
 namespace {
 
 constexpr int kSlotIdsPerLaunch = 256;
@@ -215,7 +237,7 @@ extern "C" int moe_merge_weights(const moe_pool* local, const int32_t* ids_host,
   rc = copy_pool_experts(local, ids_host, n_ids, dst, s, plan);
   if (rc) return rc;
   if (ready) MOE_HIP_CHECK(hipEventRecord(as_event(ready), s));
-  return MOE_OK;
+  return debug_check(MOE_OK, "moe_merge_weights", s, nullptr);
 }
 
 extern "C" int moe_prefetch_layer(const moe_pool* remote, const int32_t* ids_host, int n_ids,
@@ -236,7 +258,7 @@ extern "C" int moe_prefetch_layer(const moe_pool* remote, const int32_t* ids_hos
   rc = copy_pool_experts(remote, ids_host, n_ids, dst, s, plan);
   if (rc) return rc;
   if (ready) MOE_HIP_CHECK(hipEventRecord(as_event(ready), s));
-  return MOE_OK;
+  return debug_check(MOE_OK, "moe_prefetch_layer", s, nullptr);
 }
 
 extern "C" int moe_event_create(moe_event_t* ev, int timing) {

@@ -64,8 +64,17 @@ enum {
   MOE_ERR_ARG = -1,         /* invalid argument; nothing enqueued */
   MOE_ERR_UNSUPPORTED = -2, /* valid, but outside what the kernels support; nothing enqueued */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or too small; nothing enqueued */
-  MOE_ERR_HIP = -4          /* a HIP runtime call failed; see moe_last_error() */
+  MOE_ERR_HIP = -4,         /* a HIP runtime call failed; see moe_last_error() */
+  MOE_ERR_STATUS = -5       /* debug mode only: the call's kernels set a status bit */
 };
+
+/*
+ * Debug mode: with MOE_DEBUG_SYNC set in the environment (to anything but "" or "0"),
+ * every call that enqueues work synchronises its stream before returning.  A kernel that
+ * failed then returns MOE_ERR_HIP, and a set bit of the call's status word (when it takes
+ * one) MOE_ERR_STATUS, each with a description in moe_last_error(); the failing call is
+ * the one that returns.  Off by default: the calls then only enqueue.
+ */
 
 /* bits of the device status word */
 #define MOE_STATUS_NONFINITE_LOGIT 1 /* a router logit was NaN or +-inf */

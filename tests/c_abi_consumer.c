@@ -34,6 +34,52 @@ int main(void) {
             MOE_ERR_ARG,
         "unknown dtype rejected");
   check(moe_route(NULL, 4, 8, 9, NULL, NULL, NULL, NULL) == MOE_ERR_ARG, "k > E rejected");
+  check(moe_route(NULL, 4, 2048, 2, NULL, NULL, NULL, NULL) == MOE_ERR_UNSUPPORTED,
+        "E above the kernel limit rejected");
+  check(moe_permute_noalloc(NULL, 2, 2048, 2, NULL, 8, MOE_BF16, NULL, NULL, NULL, NULL, NULL,
+                            NULL, NULL) == MOE_ERR_UNSUPPORTED,
+        "moe_permute_noalloc: E above the limit rejected");
+  check(moe_grouped_swiglu_combine(NULL, NULL, NULL, 4, 2, NULL, 8, 64, 32, MOE_F32, NULL, NULL,
+                                   0, NULL, NULL, NULL) == MOE_ERR_UNSUPPORTED,
+        "moe_grouped_swiglu_combine: f32 rejected");
+  check(moe_combine(NULL, NULL, NULL, 4, 65, 8, NULL, NULL) == MOE_ERR_UNSUPPORTED,
+        "moe_combine: k above the limit rejected");
+
+  /* the merge's id checks read the host id array: unsorted, out of range, too many ids */
+  {
+    moe_pool pool;
+    moe_wbuf buf;
+    int32_t slots[8];
+    static char fake_base[1];
+    const int32_t unsorted[2] = {3, 1};
+    const int32_t out_of_range[2] = {0, 8};
+    const int32_t too_many[5] = {0, 1, 2, 3, 4};
+    pool.base = fake_base;
+    pool.expert_bytes = 96;
+    pool.first_expert = 0;
+    pool.n_experts = 4;
+    buf.base = fake_base;
+    buf.expert_bytes = 96;
+    buf.n_slots = 4;
+    buf.n_experts = 8;
+    buf.slot_of = slots;
+    check(moe_merge_weights(&pool, unsorted, 2, &buf, NULL, NULL, NULL, MOE_COPY_SDMA) ==
+              MOE_ERR_ARG, "merge: unsorted ids rejected");
+    check(moe_merge_weights(&pool, out_of_range, 2, &buf, NULL, NULL, NULL, MOE_COPY_SDMA) ==
+              MOE_ERR_ARG, "merge: id out of range rejected");
+    check(moe_prefetch_layer(&pool, too_many, 5, &buf, NULL, NULL, NULL, MOE_COPY_SDMA) ==
+              MOE_ERR_ARG, "prefetch: more ids than slots rejected");
+    check(moe_prefetch_layer(&pool, unsorted, 2, &buf, NULL, NULL, NULL, 3) == MOE_ERR_ARG,
+          "prefetch: unknown copy mode rejected");
+    check(strstr(moe_last_error(), "moe_prefetch_layer") != NULL, "error text names the call");
+  }
+  {
+    moe_phys_t ph = NULL;
+    size_t zero = 0;
+    void* va = NULL;
+    check(moe_vmm_create(0, 0, &ph) == MOE_ERR_ARG, "vmm: empty block rejected");
+    check(moe_vmm_map(0, NULL, &zero, 1, &va) == MOE_ERR_ARG, "vmm: map without blocks rejected");
+  }
 
   if (failures == 0) printf("ok %s\n", v);
   return failures == 0 ? 0 : 1;

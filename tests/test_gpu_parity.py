@@ -571,3 +571,27 @@ def test_combine_in_epilogue_r1_prefill_t16384():
         check_y_tokens(cfg, L, _sample(cfg.T, 64, 17))
     finally:
         L.close()
+
+
+def test_debug_sync_mode(monkeypatch):
+    """MOE_DEBUG_SYNC=1: every call synchronises; results are unchanged, and a status bit set
+    by a call's kernels comes back from that very call as MOE_ERR_STATUS."""
+    from grouped_gemm_weights_amd import binding as B
+    cfg = synth.MoEConfig("bf16_debug_sync", T=80, H=128, I=64, E=12, k=3, dtype="bf16",
+                          n_local=3, seed=41)
+    log(f"case {cfg.name}")
+    L = build_layer(cfg)
+    L.forward(half=0)
+    ref = L.outputs()
+    monkeypatch.setenv("MOE_DEBUG_SYNC", "1")
+    L.forward(half=1)
+    out = L.outputs()
+    assert out["status"] == 0
+    assert out["y"].tobytes() == ref["y"].tobytes()
+    logits = synth.logits(cfg)
+    logits[3, 5] = np.nan
+    L.set_inputs(synth.activations(cfg), logits)
+    with pytest.raises(B.MoEError) as e:
+        L.route_permute()
+    assert e.value.code == B.MOE_ERR_STATUS
+    assert "moe_route" in str(e.value) and "non-finite" in str(e.value)
