@@ -80,6 +80,8 @@ def parse():
                    help="pipelines: cut the main pull into this many expert-aligned chunks, each "
                         "with its own ready event; the grouped GEMM runs per chunk as it lands")
     p.add_argument("--workload-steps", type=int, default=10)
+    p.add_argument("--no-library-baseline", dest="library_baseline", action="store_false",
+                   help="skip timing the vendor BLAS on the same per-expert GEMMs")
     p.add_argument("--pipeline-steps", type=int, default=3)
     p.add_argument("--calibrate", action="store_true",
                    help="run only a plain streaming kernel of known size (moe_residual_add over "
@@ -427,10 +429,51 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def library_baseline(L, cfg, reps=3):
+    """The same grouped GEMM work done by the vendor BLAS (hipBLASLt through torch's
+    F.linear), one call per active expert and projection -- [rows, H] x [2I, H]^T for gate
+    and up together, then [rows, I] x [H, I]^T -- on the weight bytes of the layer's pools,
+    SiLU left out.  Context for the grouped kernel's time, not part of the path."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+    H, I, k = cfg.H, cfg.I, cfg.k
+    counts = L.counts.cpu().numpy()
+    offs = L.offsets.cpu().numpy()
+    xp = L.x.index_select(0, (L.src_of // k).long())          # x_perm, built outside the clock
+    hs = torch.empty((L.R, I), dtype=xp.dtype, device=xp.device)
+    experts = [int(e) for e in np.nonzero(counts)[0]]
+    mats = []
+    for e in experts:
+        blk = L.expert_block(e)
+        mats.append((int(offs[e]), int(offs[e + 1]), blk[: 2 * H * I].view(2 * I, H),
+                     blk[2 * H * I:].view(H, I)))
+    torch.cuda.synchronize()
+
+    def run():
+        for lo, hi, wgu, wd in mats:
+            F.linear(xp[lo:hi], wgu)
+            F.linear(hs[lo:hi], wd)
+
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    flop = 6.0 * H * I * L.R
+    del xp, hs, mats
+    return {"kind": "hipBLASLt via torch F.linear, one call per active expert and projection "
+                    "(gate and up as one [2I, H] matrix; SiLU left out)",
+            "calls": 2 * len(experts), "ms": round(ms, 3),
+            "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1)}
+
+
 def layer_summary(r):
     """The figures of a single-layer record that matter beside the headline."""
     keep = ("value", "unit", "ms_per_step", "roofline", "breakdown_ms", "timing", "copy",
-            "active_experts", "gemm_TFLOPs", "hbm_frac", "mfma_frac")
+            "active_experts", "gemm_TFLOPs", "hbm_frac", "mfma_frac", "library_baseline")
     out = {k: r[k] for k in keep if k in r}
     out["config"] = {k: r["config"][k] for k in ("tokens", "remote_fetch", "merge", "gather",
                                                   "copy_engine", "combine")}
@@ -629,6 +672,10 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
     }
     if alt is not None:
         result["other_copy_engine"] = alt
+    if args.library_baseline and not remote_on_host:
+        lb = library_baseline(L, cfg)
+        lb["grouped_kernel_speedup"] = round(lb["ms"] / gemm_ms, 3)
+        result["library_baseline"] = lb
     if headline:
         result["inputs_sha256"] = input_digests(cfg, local, remote)
         result["_y"] = L.y.detach().cpu().numpy()
