@@ -290,6 +290,9 @@ def calibrate():
 
 
 GEMM_SOURCE = os.path.join(ROOT, "grouped_gemm_weights_amd", "csrc", "grouped_swiglu.hip")
+# the short bench run the counter passes profile (one workload, nothing timed beside it)
+PROFILE_ARGS = ("--config {cfg} --steps 2 --warmup 1 --workloads none --no-cpu-baseline "
+                "--no-library-baseline --alt-steps 0")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_swiglu_traffic.json")
 # kernels of one moe_grouped_swiglu call
 GROUPED_KERNELS = ("plan_kernel", "gemm_stream_kernel", "gemm_wide_kernel")
@@ -355,9 +358,9 @@ def write_traffic(prof_dir, workloads):
             "hbm_bytes_per_call": rd + wr,
             "commands": [
                 f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch_{cfg} -o run -- "
-                f"python3 bench.py --config {cfg} --steps 2 --warmup 1 --no-cpu-baseline",
+                f"python3 bench.py {PROFILE_ARGS.format(cfg=cfg)}",
                 f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write_{cfg} -o run -- "
-                f"python3 bench.py --config {cfg} --steps 2 --warmup 1 --no-cpu-baseline",
+                f"python3 bench.py {PROFILE_ARGS.format(cfg=cfg)}",
             ],
         }
     rec["calibration"]["commands"] = [
