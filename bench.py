@@ -133,6 +133,25 @@ def cpu_baseline_bulk(cfg, blocks, y_gpu, single_thread_tokens=0):
         out["single_thread"] = {"value": round(n / d1, 4), "unit": "tokens/s",
                                 "sample": f"the same path on the first {n} tokens, one BLAS "
                                           f"thread, {d1:.1f} s"}
+    # the tiny fp32 layer (64 tokens, 8 experts) through the same path, whole, at full and
+    # at one BLAS thread (its weights are drawn on the host)
+    from threadpoolctl import threadpool_limits
+    tc = synth.config("tiny_fp32_t64")
+    tb = synth.pool_np(tc, 0, range(tc.E))
+    tx, tl = synth.activations(tc), synth.logits(tc)
+    tiny = {}
+    for name, lim in (("all_threads", None), ("single_thread", 1)):
+        with threadpool_limits(limits=lim):
+            reps, t2 = 0, time.perf_counter()
+            while True:
+                O.moe_layer(tx, tl, tc.k, lambda e: tb[e], tc.H, tc.I, round_h=False,
+                            dtype=np.float32)
+                reps += 1
+                if time.perf_counter() - t2 > 0.5:
+                    break
+            d2 = (time.perf_counter() - t2) / reps
+        tiny[name] = {"value": round(tc.T / d2, 1), "unit": "tokens/s", "ms": round(d2 * 1e3, 3)}
+    out["tiny_fp32_t64"] = tiny
     return out
 
 

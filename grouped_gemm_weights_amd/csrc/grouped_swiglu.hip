@@ -34,6 +34,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct Tile {
   int32_t expert;
@@ -289,7 +290,7 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
   // stages in flight from global memory: two for tiles of at most 64 rows (their short K
   // iterations would not cover the latency of one), else one (no registers left for more)
   constexpr int RING = (MI == 2 || MI == 0) ? 2 : 1;
-  uint4 ra[RING][CHA], rb[RING][CHB];
+  u32x4_t ra[RING][CHA], rb[RING][CHB];
   bf16x8_t pa[MW], pb[NJ], qa[MW], qb[NJ]; // operands of two consecutive K steps
 
   // one global chunk load into ring slot rs (chunk t: A chunks first, then B); past K
@@ -300,22 +301,22 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
                                            a_base + (a_off[(t) % CHA] + 2u * (k0)))    \
                          : ((DUAL && ((t) - CHA) % CHB >= CHB / 2) ? B1 : B0) +        \
                                (b_off[((t) - CHA) % CHB] + (k0));                      \
-    uint4 v_;                                                                          \
+    u32x4_t v_;                                                                        \
     if (KFULL) {                                                                       \
-      v_ = *reinterpret_cast<const uint4*>(src_);                                      \
+      v_ = *reinterpret_cast<const u32x4_t*>(src_);                                    \
     } else {                                                                           \
-      v_ = make_uint4(0, 0, 0, 0);                                                     \
-      if ((k0) + kc * 8 < K) v_ = *reinterpret_cast<const uint4*>(src_);               \
+      v_ = u32x4_t{0, 0, 0, 0};                                                        \
+      if ((k0) + kc * 8 < K) v_ = *reinterpret_cast<const u32x4_t*>(src_);             \
     }                                                                                  \
     if ((t) < CHA) ra[rs][(t) % CHA] = v_; else rb[rs][((t) - CHA) % CHB] = v_;        \
   } while (0)
 #define W_DSW(t, buf, rs)                                                              \
   do {                                                                                 \
     if ((t) < CHA)                                                                     \
-      *reinterpret_cast<uint4*>(As + (buf) * STAGE + st_off + ((t) % CHA) * RSTEP * LDS_LD) = \
+      *reinterpret_cast<u32x4_t*>(As + (buf) * STAGE + st_off + ((t) % CHA) * RSTEP * LDS_LD) = \
           ra[rs][(t) % CHA];                                                           \
     else                                                                               \
-      *reinterpret_cast<uint4*>(Bs + (buf) * STAGE + st_off +                          \
+      *reinterpret_cast<u32x4_t*>(Bs + (buf) * STAGE + st_off +                        \
                                 (((t) - CHA) % CHB) * RSTEP * LDS_LD) = rb[rs][((t) - CHA) % CHB]; \
   } while (0)
   // one operand fragment read (slot t: A row blocks first, then B column blocks) of K step s

@@ -53,3 +53,21 @@ def test_traffic_record_scaling_and_source_guard(tmp_path, monkeypatch):
     assert bench.traffic_from_profiles("w") == w
     monkeypatch.setattr(bench, "_source_sha256", lambda: "0" * 64)
     assert bench.traffic_from_profiles("w") is None
+
+
+def test_cpu_baseline_bulk_leg():
+    """bench.py's cpu_baseline leg on the tiny fp32 layer: it runs the oracle's bulk float32
+    path over the whole layer, reports the threads it used, and compares the output it is
+    handed (here the float64 oracle's own) to its own result."""
+    import numpy as np
+    from grouped_gemm_weights_amd import synth
+    from oracle import moe as O
+    cfg = synth.config("tiny_fp32_t64")
+    blocks = {e: b for e, b in enumerate(synth.pool_np(cfg, 0, range(cfg.E)))}
+    ref = O.moe_layer(synth.activations(cfg), synth.logits(cfg), cfg.k, lambda e: blocks[e],
+                      cfg.H, cfg.I, False)
+    r = bench.cpu_baseline_bulk(cfg, blocks, ref["y"], 8)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
+    assert r["cores"] >= 1 and r["single_thread"]["value"] > 0
+    assert r["gpu_vs_cpu_max_err_over_rms"] <= 1e-5
+    assert set(r["tiny_fp32_t64"]) == {"all_threads", "single_thread"}
