@@ -198,6 +198,33 @@ def test_prefill_tile_modes_at_row_boundaries(fused):
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
+def test_prefill_multi_tile_experts(fused):
+    """Experts of 511, 512, 513, 1024 and 1025 rows (k = 1): a full 256-row tile and a 255-row
+    one, exactly two, two plus a one-row tail (a 64-row column-split tile), four, four plus one
+    row; H = 256 and I = 192 as above.  Every row is checked."""
+    counts = [511, 512, 513, 1024, 1025, 3, 0]
+    T = sum(counts)
+    cfg = synth.MoEConfig("bf16_multi_tile", T=T, H=256, I=192, E=len(counts), k=1, dtype="bf16",
+                          n_local=2, seed=29)
+    log(f"case {cfg.name} fused={fused}")
+    L = build_layer(cfg, fused_gather=fused)
+    expert_of = np.repeat(np.arange(cfg.E), counts)
+    np.random.default_rng(30).shuffle(expert_of)
+    logits = synth.logits(cfg)
+    logits[np.arange(T), expert_of] += 50.0
+    L.set_inputs(synth.activations(cfg), logits)
+    L.forward(half=0)
+    out = L.outputs()
+    assert out["status"] == 0
+    np.testing.assert_array_equal(out["counts"], counts)
+    check_routing(cfg, out, logits)
+    ref = O.moe_layer(synth.activations(cfg), logits, cfg.k, weights_fn(L), cfg.H, cfg.I, True)
+    e_yp, e_y = rel_err(out["y_perm"], ref["y_perm"]), rel_err(out["y"], ref["y"])
+    log(f"{cfg.name}: y_perm err/rms {e_yp:.3e}, y err/rms {e_y:.3e}")
+    assert e_yp <= TOL["bf16"] and e_y <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
 def test_decode_tiles_at_row_boundaries(fused):
     """Decode-path layer (at most 4 rows per expert on average) with expert row counts around
     the 16-row stream tile (1, 15, 16, 17, 32, 33), k = 1; H = 320 and I = 192 give both stream
