@@ -420,6 +420,21 @@ def test_r1_decode_t64(stitched):
         L.close()
 
 
+def test_r1_decode_t64_remote_pool_on_host():
+    """The remote share (192 experts, 16.9 GB) in pinned host memory: the routed pull crosses
+    PCIe into the stitched half.  Every row and every token is checked."""
+    cfg = synth.config("r1_decode_t64")
+    log(f"case {cfg.name} remote pool in pinned host memory")
+    L = build_layer(cfg, stitched=True, remote_on_host=True)
+    try:
+        assert not L._remote_t.is_cuda and L._remote_t.is_pinned()
+        _run(L)
+        _, n = check_rows(cfg, L, range(cfg.R), range(cfg.T))
+        assert n == cfg.R
+    finally:
+        L.close()
+
+
 def test_r1_decode_t64_dwdp3_split():
     """The 3-rank split: 86 local experts, 170 fetched; stitched merge."""
     cfg = synth.config("r1_decode_t64_dwdp3")
