@@ -126,27 +126,6 @@ def check_full(cfg, L, layer: int = 0):
     return out, ref
 
 
-def check_sampled(cfg, L, tokens, layer: int = 0, x=None, logits=None, check_xperm=True):
-    """Full routing/permutation parity, x_perm bitwise, y and y_perm on sampled tokens."""
-    out = L.outputs()
-    assert out["status"] == 0, f"device status {out['status']}"
-    x = synth.activations(cfg, layer) if x is None else x
-    logits = synth.logits(cfg, layer) if logits is None else logits
-    idx, w, src_of, row_of = check_routing(cfg, out, logits)
-    if check_xperm:
-        assert np.array_equal(out["x_perm"], np.asarray(x)[src_of // cfg.k])
-    ref = O.moe_layer_tokens(x, logits, cfg.k, weights_fn(L), cfg.H, cfg.I,
-                             round_h=cfg.dtype == "bf16", tokens=tokens)
-    tol = TOL[cfg.dtype]
-    e_y = rel_err(out["y"][tokens], ref["y"])
-    rows = np.array([row_of[t * cfg.k + j] for t in tokens for j in range(cfg.k)])
-    yp_ref = ref["expert_out"].reshape(len(tokens) * cfg.k, cfg.H)
-    e_yp = rel_err(out["y_perm"][rows], yp_ref)
-    log(f"{cfg.name}: {len(tokens)} sampled tokens: y err/rms {e_y:.3e}, y_perm err/rms {e_yp:.3e}")
-    assert e_y <= tol and e_yp <= tol
-    return out
-
-
 # ----------------------------------------------------------------------------
 # full-size checks: many rows, each expert's weights read back and decoded once
 # ----------------------------------------------------------------------------
