@@ -5,9 +5,10 @@ One step = one pass of the whole hot path over one batch of synthetic input,
 with the weight pools and inputs already resident in HBM:
 
     route -> permute (counts, offsets, permutation, row gather)
-    -> read the per-expert counts back (the routed remote set depends on them)
-    -> copy stream: merge the local experts into the merged buffer half and
-       prefetch the routed remote experts from the stand-in peer pool (SDMA)
+    -> copy stream (after an event on the permute): merge the local experts
+       into the merged buffer half and pull the routed remote experts from the
+       stand-in peer pool, the routed set read from the counts on the device
+       (--remote routed reads the counts back to the host and pulls that set)
     -> compute stream waits for the copies -> grouped SwiGLU GEMM -> combine
 
 Steps alternate between the two halves of the double buffer.  The default
@@ -39,8 +40,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="r1_decode_t64")
-    p.add_argument("--remote", choices=["routed", "all"], default="routed",
-                   help="prefetch only the routed remote experts, or the whole remote share")
+    p.add_argument("--remote", choices=["device", "routed", "all"], default="device",
+                   help="prefetch only the routed remote experts (device: picked on the device "
+                        "from the counts, nothing read back; routed: after a count read-back), "
+                        "or the whole remote share")
     p.add_argument("--copy-mode", choices=["sdma", "any", "kernel"], default="kernel",
                    help="any: hipMemcpyDefault (the runtime's copy path); sdma: the no-compute-unit "
                         "copy kind; kernel: the library's copy kernel on --copy-blocks workgroups")
@@ -431,8 +434,12 @@ def main():
             c = synth.config(name[: -len("_host_pool")] if host_pool else name)
             t0 = time.perf_counter()
             if host_pool:
-                # the offload variant: every pull crosses PCIe, so a few steps suffice
-                r = bench_layer(args, c, dev, copy_mode, 3, 1, 0, remote_on_host=True)
+                # the offload variant: every pull crosses PCIe, so a few steps suffice; a host
+                # pool is pulled by the copy engine after the count read-back
+                ha = argparse.Namespace(**vars(args))
+                if ha.remote == "device":
+                    ha.remote = "routed"
+                r = bench_layer(ha, c, dev, copy_mode, 3, 1, 0, remote_on_host=True)
                 wl[name] = layer_summary(r)
             elif c.layers == 1:
                 r = bench_layer(args, c, dev, copy_mode, args.workload_steps, 2, 0)
@@ -541,6 +548,11 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
     mk = lambda: [B.moe_event_create(True) for _ in range(nev)]
     ev = {k: mk() for k in ("start", "rp_end", "gemm0", "gemm1", "end", "copy0", "copy1")}
     nch = max(0, args.chunks)
+    on_device = args.remote == "device"
+    if on_device and nch > 0:
+        raise SystemExit("--remote device is not chunked")
+    if on_device:
+        alt_steps = 0              # the device-routed pull always runs on the copy kernel
     gev = [{"g0": [B.moe_event_create(True) for _ in range(nch + 1)],
             "g1": [B.moe_event_create(True) for _ in range(nch + 1)]} for _ in range(nev)]
 
@@ -551,7 +563,14 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
         L.route_permute()
         if timed:
             B.moe_event_record(ev["rp_end"][i], cs)
-        ids = L.routed_ids() if args.remote == "routed" else list(range(cfg.E))
+        if on_device:
+            ids = None
+            # the copy stream's wait for the permute, ahead of its start event, so the copy's
+            # time counts from the routing being known (the host does not wait here)
+            B.moe_event_record(L.counts_ready, cs)
+            B.moe_stream_wait_event(ps, L.counts_ready)
+        else:
+            ids = L.routed_ids() if args.remote == "routed" else list(range(cfg.E))
         if timed:
             B.moe_event_record(ev["copy0"][i], ps)
         if nch > 0:
@@ -560,7 +579,10 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
                 B.moe_event_record(ev["copy1"][i], ps)
                 B.moe_event_record(ev["end"][i], cs)
             return ids
-        L.fill_half(h, ids)
+        if on_device:
+            L.fill_half_routed_on_device(h)
+        else:
+            L.fill_half(h, ids)
         if timed:
             B.moe_event_record(ev["copy1"][i], ps)
         B.moe_stream_wait_event(cs, L.ready[h])
@@ -632,6 +654,8 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
 
     counts = L.counts.cpu().numpy()
     n_active = int((counts > 0).sum())
+    if ids is None:                 # the device-routed set: every local expert and the routed rest
+        ids = list(range(cfg.n_local)) + [e for e in range(cfg.n_local, cfg.E) if counts[e] > 0]
     eb = synth.expert_block_bytes(cfg)
     R = cfg.T * cfg.k
     # weights read + x_perm + y_perm; with the combine in the epilogue: + x rows read through

@@ -32,7 +32,8 @@ def copy_kernel_on(n_blocks: int) -> int:
 EXPORTS = (
     "moe_route", "moe_permute_workspace_size", "moe_permute", "moe_permute_noalloc",
     "moe_merge_weights",
-    "moe_prefetch_layer", "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu",
+    "moe_prefetch_layer", "moe_prefetch_routed", "moe_grouped_swiglu_workspace_size",
+    "moe_grouped_swiglu",
     "moe_grouped_swiglu_range", "moe_grouped_swiglu_gathered", "moe_grouped_swiglu_combine",
     "moe_combine", "moe_dense_gemm", "moe_residual_add", "moe_event_create",
     "moe_event_destroy", "moe_event_record", "moe_event_elapsed_ms", "moe_stream_wait_event",
@@ -71,6 +72,7 @@ def _load() -> ctypes.CDLL:
         "moe_permute_noalloc": [P, I, I, I, P, I, I, P, P, P, P, P, P, P],
         "moe_merge_weights": [ctypes.POINTER(MoePool), P, I, ctypes.POINTER(MoeWbuf), P, P, P, I],
         "moe_prefetch_layer": [ctypes.POINTER(MoePool), P, I, ctypes.POINTER(MoeWbuf), P, P, P, I],
+        "moe_prefetch_routed": [ctypes.POINTER(MoePool), P, ctypes.POINTER(MoeWbuf), P, P, P, P, I],
         "moe_grouped_swiglu_workspace_size": [I, I, I, I, I, PSZ],
         "moe_grouped_swiglu": [P, P, I, I, I, I, I, ctypes.POINTER(MoeWbuf), P, SZ, P, P, P],
         "moe_grouped_swiglu_range": [P, P, I, I, I, I, I, ctypes.POINTER(MoeWbuf), I, I, P, SZ, P, P, P],
@@ -187,6 +189,14 @@ def moe_prefetch_layer(remote: MoePool, ids: Sequence[int], dst: MoeWbuf, copy_s
                                                         ctypes.byref(dst),
                                                         stream_handle(copy_stream), wait_free,
                                                         ready, copy_mode))
+
+
+def moe_prefetch_routed(remote: MoePool, counts, dst: MoeWbuf, copy_stream=None,
+                        counts_ready=None, wait_free=None, ready=None, max_blocks: int = 0):
+    _check("moe_prefetch_routed", lib.moe_prefetch_routed(ctypes.byref(remote), ptr(counts),
+                                                          ctypes.byref(dst),
+                                                          stream_handle(copy_stream), counts_ready,
+                                                          wait_free, ready, max_blocks))
 
 
 def moe_grouped_swiglu_workspace_size(R, E, H, I, dtype) -> int:

@@ -164,6 +164,64 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const u32x4* __restr
   }
 }
 
+// The routed pull with the expert set read on the device.  A chunk is the kCopyThreads *
+// kCopyUnroll 16-byte units a workgroup moves at once; work unit c is kRoutedChunks
+// consecutive chunks (group c % gpe) of pool expert c / gpe.  Workgroups take units
+// c = blockIdx.x, blockIdx.x + gridDim.x, ... and skip those of experts that received no
+// tokens; reading that count is one dependent load before a unit's copies start, so a unit
+// holds several chunks to spread it (one chunk per unit made the pull 7 % slower than the
+// host-routed per-run copies).  The slot map entries of the pool's experts (the slot, or -1
+// for an expert with no tokens, whose slot is left as it was) are written by the first
+// threads of the grid.
+constexpr int kRoutedChunks = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_routed_kernel(
+    const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t eb16, int64_t gpe, int first,
+    int n, const int32_t* __restrict__ counts, int32_t* __restrict__ slot_of) {
+  constexpr int64_t kChunk = static_cast<int64_t>(kCopyThreads) * kCopyUnroll;
+  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * kCopyThreads;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x; q < n;
+       q += nthreads) {
+    const int e = first + static_cast<int>(q);
+    slot_of[e] = counts[e] > 0 ? e : -1;
+  }
+  const int64_t units = static_cast<int64_t>(n) * gpe;
+  for (int64_t c = blockIdx.x; c < units; c += gridDim.x) {
+    const int p = static_cast<int>(c / gpe);
+    if (counts[first + p] <= 0) continue;
+    const u32x4* __restrict__ from = src + static_cast<int64_t>(p) * eb16;
+    u32x4* __restrict__ to = dst + static_cast<int64_t>(first + p) * eb16;
+    const int64_t c0 = (c % gpe) * kRoutedChunks * kChunk;   // first unit of the group
+    for (int g = 0; g < kRoutedChunks; ++g) {
+      const int64_t chunk0 = c0 + g * kChunk;
+      const int64_t base = chunk0 + threadIdx.x;
+      u32x4 v[kCopyUnroll];
+      if (chunk0 + kChunk <= eb16) {
+        // a whole chunk (a workgroup-uniform test): straight-line loads, then stores, so the
+        // next chunk's loads issue without waiting for these stores
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+          v[u] = __builtin_nontemporal_load(from + base + static_cast<int64_t>(u) * kCopyThreads);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+          __builtin_nontemporal_store(v[u], to + base + static_cast<int64_t>(u) * kCopyThreads);
+      } else if (chunk0 < eb16) {
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
+          v[u] = u32x4{0, 0, 0, 0};
+          if (i < eb16) v[u] = __builtin_nontemporal_load(from + i);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
+          if (i < eb16) __builtin_nontemporal_store(v[u], to + i);
+        }
+      }
+    }
+  }
+}
+
 int copy_run(void* to, const void* from, size_t bytes, const CopyPlan& plan, hipStream_t s) {
   const bool aligned = (reinterpret_cast<uintptr_t>(to) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(from) % 16 == 0) && (bytes % 16 == 0);
@@ -301,3 +359,55 @@ extern "C" int moe_stream_wait_event(moe_stream_t stream, moe_event_t ev) {
 extern "C" const char* moe_last_error(void) { return moe::last_error().c_str(); }
 
 extern "C" const char* moe_version(void) { return "moe-gfx950 0.1"; }
+
+extern "C" int moe_prefetch_routed(const moe_pool* remote, const int32_t* counts, moe_wbuf* dst,
+                                   moe_stream_t copy_stream, moe_event_t counts_ready,
+                                   moe_event_t wait_free, moe_event_t ready, int max_blocks) {
+  using namespace moe;
+  if (injected_fault("prefetch"))
+    return fail(MOE_ERR_HIP, "moe_prefetch_routed: fault injected (MOE_INJECT_FAULT=prefetch)");
+  int rc = check_ids("moe_prefetch_routed", nullptr, 0, dst);
+  if (rc) return rc;
+  rc = check_pool("moe_prefetch_routed", remote, dst);
+  if (rc) return rc;
+  if (!counts || !dst->slot_of) return fail(MOE_ERR_ARG, "moe_prefetch_routed: null pointer");
+  if (max_blocks < 0) return fail(MOE_ERR_ARG, "moe_prefetch_routed: max_blocks %d", max_blocks);
+  const int64_t first = remote->first_expert, n = remote->n_experts;
+  if (first + n > dst->n_experts || first + n > dst->n_slots)
+    return fail(MOE_ERR_ARG, "moe_prefetch_routed: experts [%lld, %lld) need slots up to their "
+                "ids (buffer: %d experts, %d slots)", static_cast<long long>(first),
+                static_cast<long long>(first + n), dst->n_experts, dst->n_slots);
+  if (n > 65535) return fail(MOE_ERR_UNSUPPORTED, "moe_prefetch_routed: %lld experts", static_cast<long long>(n));
+  const int64_t eb = dst->expert_bytes;
+  if (eb % 16 != 0 || reinterpret_cast<uintptr_t>(remote->base) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(dst->base) % 16 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_prefetch_routed: expert blocks of %lld bytes or bases "
+                "not 16-byte aligned", static_cast<long long>(eb));
+  if (n > 0) {
+    hipPointerAttribute_t attr;
+    MOE_HIP_CHECK(hipPointerGetAttributes(&attr, remote->base));
+    if (attr.type == hipMemoryTypeHost)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_prefetch_routed: the pool is in host memory (pull it "
+                  "with moe_prefetch_layer after reading the counts back)");
+  }
+  hipStream_t s = as_stream(copy_stream);
+  if (counts_ready) MOE_HIP_CHECK(hipStreamWaitEvent(s, as_event(counts_ready), 0));
+  if (wait_free) MOE_HIP_CHECK(hipStreamWaitEvent(s, as_event(wait_free), 0));
+  if (n > 0) {
+    const int64_t eb16 = eb / 16;
+    const int64_t gpe = ceil_div64(eb16, static_cast<int64_t>(kCopyThreads) * kCopyUnroll *
+                                             kRoutedChunks);
+    const int64_t units = n * gpe;
+    // one workgroup per unit unless bounded (the slot map needs ceil(n / kCopyThreads) at most,
+    // which a bound of one workgroup still covers through the loop)
+    int64_t blocks = max_blocks > 0 ? std::min<int64_t>(max_blocks, units) : units;
+    blocks = std::min<int64_t>(blocks, kCopyMaxBlocks);
+    hipLaunchKernelGGL(copy_routed_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCopyThreads),
+                       0, s, static_cast<const u32x4*>(remote->base),
+                       static_cast<u32x4*>(dst->base), eb16, gpe, static_cast<int>(first),
+                       static_cast<int>(n), counts, dst->slot_of);
+    MOE_LAUNCH_CHECK("moe_prefetch_routed: copy");
+  }
+  if (ready) MOE_HIP_CHECK(hipEventRecord(as_event(ready), s));
+  return debug_check(MOE_OK, "moe_prefetch_routed", s, nullptr);
+}

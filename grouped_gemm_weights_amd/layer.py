@@ -121,6 +121,7 @@ class MoELayer:
         self.copy_stream = copy_stream or torch.cuda.Stream(device=d)
         self.ready = [B.moe_event_create(False) for _ in range(n_halves)]
         self.free = [B.moe_event_create(False) for _ in range(n_halves)]
+        self.counts_ready = B.moe_event_create(False)
         self.local_pool = None
         self.remote_pool = None
         self.last_ids = None
@@ -228,6 +229,22 @@ class MoELayer:
                              wait_free=None, ready=self.ready[half], copy_mode=self.copy_mode)
         self.last_ids = list(ids)
 
+    def fill_half_routed_on_device(self, half: int, wait_free: bool = True) -> None:
+        """Copy stream: the local experts (merge of ids 0 .. n_local - 1) and the routed remote
+        experts decided on the device from this step's counts (slot = expert id), with no count
+        read-back.  Call after route_permute."""
+        cfg = self.cfg
+        local = self.stitched_local_pools[half] if self.stitched_local_pools else self.local_pool
+        B.moe_event_record(self.counts_ready, self.compute_stream)
+        B.moe_merge_weights(local, range(cfg.n_local), self.wbufs[half], self.copy_stream,
+                            wait_free=self.free[half] if wait_free else None, ready=None,
+                            copy_mode=self.copy_mode)
+        kernel = (self.copy_mode & 0xFF) == B.MOE_COPY_KERNEL
+        B.moe_prefetch_routed(self.remote_pool, self.counts, self.wbufs[half], self.copy_stream,
+                              counts_ready=self.counts_ready, ready=self.ready[half],
+                              max_blocks=(self.copy_mode >> 8) if kernel else 0)
+        self.last_ids = None                  # the expert set never reaches the host
+
     def expert_compute(self, half: int) -> None:
         """Compute stream: wait for the half, grouped SwiGLU GEMM, combine, release the half."""
         cs = self.compute_stream
@@ -237,10 +254,18 @@ class MoELayer:
 
     def forward(self, half: int = 0, remote: str = "routed", chunks: int = 0, ev=None) -> None:
         """One whole layer step; remote = 'routed' (fetch only the remote experts that got
-        tokens, after a count read-back) or 'all' (fetch the whole remote share).  chunks > 0
-        splits the remote fetch into that many chunks with one ready event each, and the grouped
-        GEMM runs per chunk as its weights land (the local experts first, while the copies run)."""
+        tokens, after a count read-back), 'device' (the same set, picked on the device: no
+        read-back, nothing waits on the host) or 'all' (fetch the whole remote share).
+        chunks > 0 (not with 'device') splits the remote fetch into that many chunks with one
+        ready event each, and the grouped GEMM runs per chunk as its weights land (the local
+        experts first, while the copies run)."""
         self.route_permute()
+        if remote == "device":
+            if chunks > 0:
+                raise ValueError("the device-routed pull is not chunked")
+            self.fill_half_routed_on_device(half)
+            self.expert_compute(half)
+            return
         ids = self.routed_ids() if remote == "routed" else list(range(self.cfg.E))
         if chunks <= 0 or self.combine_in_epilogue:
             self.fill_half(half, ids)
@@ -314,9 +339,12 @@ class MoELayer:
 
     def close(self) -> None:
         self.synchronize()
-        for ev in self.ready + self.free + [e for l in getattr(self, "_cev", {}).values() for e in l]:
+        evs = self.ready + self.free + [e for l in getattr(self, "_cev", {}).values() for e in l]
+        if self.counts_ready is not None:
+            evs.append(self.counts_ready)
+        for ev in evs:
             B.moe_event_destroy(ev)
-        self.ready, self.free, self._cev = [], [], {}
+        self.ready, self.free, self._cev, self.counts_ready = [], [], {}, None
         for va, sizes in self._vmm_ranges:
             B.moe_vmm_unmap(va, sizes)
         for ph in self._vmm_phys:

@@ -237,6 +237,35 @@ int moe_prefetch_layer(const moe_pool* remote, const int32_t* ids_host, int n_id
                        moe_stream_t copy_stream, moe_event_t wait_free, moe_event_t ready,
                        int copy_mode);
 
+/*
+ * moe_prefetch_routed -- the routed pull with the expert set decided on the
+ * device, so nothing is read back to the host between the routing and the
+ * pull: on copy_stream, every expert e of the remote pool with counts[e] > 0
+ * is copied into slot e of dst, and dst->slot_of[e] is set to e, or to -1 for
+ * an expert with no tokens (whose slot keeps what it held).  The same pull
+ * as moe_prefetch_layer (DWDP explainer, "stay data-parallel" and
+ * prefetch-schedule panels) for the set that moe_permute's counts name.  The
+ * slots of the experts outside the remote pool are the caller's: a
+ * moe_merge_weights of ids 0 .. n_local - 1 before this call copies (or, for a
+ * stitched half, maps) the local experts to slots 0 .. n_local - 1 and writes
+ * -1 for every other expert.
+ *   remote       pool of experts [first, first + n) in device memory; a pool
+ *                in host memory is MOE_ERR_UNSUPPORTED (its pull stays on
+ *                moe_prefetch_layer, whose copies the copy engine runs)
+ *   counts       device i32[dst->n_experts], tokens per expert (moe_permute)
+ *   dst          merged buffer half with n_slots >= first + n: slot = expert id
+ *   counts_ready if not NULL, the stream first waits for it (the permute that
+ *                writes counts is done)
+ *   wait_free / ready as for moe_merge_weights
+ *   max_blocks   bound on the copy's workgroups (0: the library's default)
+ * Expert blocks and both bases must be 16-byte aligned (MOE_ERR_UNSUPPORTED
+ * otherwise).  MOE_INJECT_FAULT=prefetch makes the call fail as for
+ * moe_prefetch_layer.
+ */
+int moe_prefetch_routed(const moe_pool* remote, const int32_t* counts, moe_wbuf* dst,
+                        moe_stream_t copy_stream, moe_event_t counts_ready,
+                        moe_event_t wait_free, moe_event_t ready, int max_blocks);
+
 /* Workspace bytes moe_grouped_swiglu needs for R = T*k rows. */
 int moe_grouped_swiglu_workspace_size(int R, int E, int H, int I, moe_dtype dtype, size_t* bytes);
 

@@ -72,6 +72,24 @@ int main(void) {
     check(moe_prefetch_layer(&pool, unsorted, 2, &buf, NULL, NULL, NULL, 3) == MOE_ERR_ARG,
           "prefetch: unknown copy mode rejected");
     check(strstr(moe_last_error(), "moe_prefetch_layer") != NULL, "error text names the call");
+    /* the routed pull on the device: its argument checks run before any HIP call */
+    {
+      int32_t counts[8] = {0};
+      moe_pool remote = pool;
+      remote.first_expert = 4;
+      check(moe_prefetch_routed(&remote, NULL, &buf, NULL, NULL, NULL, NULL, 0) == MOE_ERR_ARG,
+            "routed prefetch: null counts rejected");
+      check(moe_prefetch_routed(&remote, counts, &buf, NULL, NULL, NULL, NULL, -1) ==
+                MOE_ERR_ARG, "routed prefetch: negative workgroup bound rejected");
+      /* experts 4..7 need slots up to 7; the buffer has 4 */
+      check(moe_prefetch_routed(&remote, counts, &buf, NULL, NULL, NULL, NULL, 0) ==
+                MOE_ERR_ARG, "routed prefetch: slot = expert id past the slots rejected");
+      check(strstr(moe_last_error(), "moe_prefetch_routed") != NULL,
+            "routed prefetch: error text names the call");
+      remote.expert_bytes = 48;
+      check(moe_prefetch_routed(&remote, counts, &buf, NULL, NULL, NULL, NULL, 0) ==
+                MOE_ERR_ARG, "routed prefetch: pool block size differing from the buffer's rejected");
+    }
   }
   {
     moe_phys_t ph = NULL;

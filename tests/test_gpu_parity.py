@@ -319,6 +319,51 @@ def test_remote_pool_in_pinned_host_memory():
     check_full(cfg, L)
 
 
+def _check_device_slot_map(cfg, L, half):
+    """slot_of after a device-routed fill: e for local experts and routed remote ones, -1 else."""
+    counts = L.counts.cpu().numpy()
+    want = np.array([e if (e < cfg.n_local or counts[e] > 0) else -1 for e in range(cfg.E)],
+                    dtype=np.int32)
+    np.testing.assert_array_equal(L.slot_maps[half].cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,n_local,zipf,stitched", [
+    (40, 128, 64, 16, 2, 4, None, False),    # prefill-like tiles
+    (40, 128, 64, 16, 2, 4, None, True),
+    (12, 1024, 200, 40, 6, 10, 1.1, False),  # decode tiles, skew: many remote experts get no token
+    (12, 1024, 200, 40, 6, 10, 1.1, True),
+    (24, 64, 32, 16, 2, 0, None, False),     # no local experts
+    (24, 64, 32, 16, 2, 16, None, False),    # no remote experts
+], ids=["prefill-copy", "prefill-stitched", "decode-skew-copy", "decode-skew-stitched",
+        "no-local", "no-remote"])
+def test_device_routed_pull(T, H, I, E, k, n_local, zipf, stitched):
+    """The routed pull decided on the device (moe_prefetch_routed): the slot map, the layer
+    against the oracle, and y bit-equal to the host-routed pull's on the other half; then a
+    second step with other logits on the same half."""
+    cfg = synth.MoEConfig(f"bf16_devroute_T{T}_E{E}_l{n_local}", T=T, H=H, I=I, E=E, k=k,
+                          dtype="bf16", n_local=n_local, seed=400 + T + E, zipf_s=zipf)
+    log(f"case {cfg.name} stitched={stitched}")
+    L = build_layer(cfg, stitched=stitched)
+    try:
+        L.forward(half=0, remote="device")
+        L.synchronize()
+        _check_device_slot_map(cfg, L, 0)
+        check_full(cfg, L)
+        y_dev = L.y.clone()
+        torch.cuda.synchronize()
+        L.forward(half=1, remote="routed")
+        L.synchronize()
+        assert torch.equal(L.y, y_dev)
+        # other logits, same half: entries of experts routed only in the first step go back to -1
+        L.set_inputs(synth.activations(cfg, 1), synth.logits(cfg, 1))
+        L.forward(half=0, remote="device")
+        L.synchronize()
+        _check_device_slot_map(cfg, L, 0)
+        check_full(cfg, L, layer=1)
+    finally:
+        L.close()
+
+
 def test_merged_buffer_bytes_and_slot_map():
     cfg = synth.MoEConfig("bf16_merge", T=40, H=64, I=32, E=20, k=3, dtype="bf16", n_local=5, seed=3)
     L = build_layer(cfg)
@@ -433,6 +478,27 @@ def test_r1_decode_t64_remote_pool_on_host():
         _run(L)
         _, n = check_rows(cfg, L, range(cfg.R), range(cfg.T))
         assert n == cfg.R
+    finally:
+        L.close()
+
+
+def test_r1_decode_t64_device_routed_pull():
+    """The R1 decode layer with the routed pull decided on the device (no count read-back):
+    every row and token, and y bit-equal to the host-routed step."""
+    cfg = synth.config("r1_decode_t64")
+    log(f"case {cfg.name} device-routed pull")
+    L = build_layer(cfg, stitched=True)
+    try:
+        L.forward(half=0, remote="device")
+        L.synchronize()
+        _check_device_slot_map(cfg, L, 0)
+        _, n = check_rows(cfg, L, range(cfg.R), range(cfg.T))
+        assert n == cfg.R
+        y_dev = L.y.clone()
+        torch.cuda.synchronize()
+        L.forward(half=1, remote="routed")
+        L.synchronize()
+        assert torch.equal(L.y, y_dev)
     finally:
         L.close()
 
