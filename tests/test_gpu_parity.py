@@ -319,12 +319,26 @@ def test_remote_pool_in_pinned_host_memory():
     check_full(cfg, L)
 
 
-def _check_device_slot_map(cfg, L, half):
-    """slot_of after a device-routed fill: e for local experts and routed remote ones, -1 else."""
+def _check_device_slot_map(cfg, L, half, check_bytes=False):
+    """slot_of after a device-routed fill: e for local experts and routed remote ones, -1 else;
+    with check_bytes, the slot of every local and routed remote expert holds exactly that
+    expert's block of its pool."""
     counts = L.counts.cpu().numpy()
     want = np.array([e if (e < cfg.n_local or counts[e] > 0) else -1 for e in range(cfg.E)],
                     dtype=np.int32)
     np.testing.assert_array_equal(L.slot_maps[half].cpu().numpy(), want)
+    if check_bytes:
+        base = L.halves[half][0]
+        if isinstance(base, int):          # a stitched half: a raw device range, viewed by torch
+
+            class _Range:
+                __cuda_array_interface__ = {"shape": (L.n_slots * L.eb,), "typestr": "|u1",
+                                            "data": (base, False), "version": 3}
+            base = torch.as_tensor(_Range(), device="cuda")
+        got = base.view(torch.uint8).reshape(L.n_slots, L.eb).cpu().numpy()
+        for e in np.nonzero(want >= 0)[0]:
+            blk = L.expert_block(int(e)).contiguous().view(torch.uint8).cpu().numpy().reshape(-1)
+            assert got[e].tobytes() == blk.tobytes(), f"slot {e}"
 
 
 @pytest.mark.parametrize("T,H,I,E,k,n_local,zipf,stitched", [
@@ -347,7 +361,7 @@ def test_device_routed_pull(T, H, I, E, k, n_local, zipf, stitched):
     try:
         L.forward(half=0, remote="device")
         L.synchronize()
-        _check_device_slot_map(cfg, L, 0)
+        _check_device_slot_map(cfg, L, 0, check_bytes=True)
         check_full(cfg, L)
         y_dev = L.y.clone()
         torch.cuda.synchronize()
@@ -358,7 +372,7 @@ def test_device_routed_pull(T, H, I, E, k, n_local, zipf, stitched):
         L.set_inputs(synth.activations(cfg, 1), synth.logits(cfg, 1))
         L.forward(half=0, remote="device")
         L.synchronize()
-        _check_device_slot_map(cfg, L, 0)
+        _check_device_slot_map(cfg, L, 0, check_bytes=True)
         check_full(cfg, L, layer=1)
     finally:
         L.close()
