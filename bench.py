@@ -44,6 +44,9 @@ def parse():
                    help="prefetch only the routed remote experts (device: picked on the device "
                         "from the counts, nothing read back; routed: after a count read-back), "
                         "or the whole remote share")
+    p.add_argument("--graph-steps", type=int, default=20,
+                   help="headline with --remote device: also replay the step captured into a HIP "
+                        "graph this many times (0: skip); reported beside the value, not as it")
     p.add_argument("--copy-mode", choices=["sdma", "any", "kernel"], default="kernel",
                    help="any: hipMemcpyDefault (the runtime's copy path); sdma: the no-compute-unit "
                         "copy kind; kernel: the library's copy kernel on --copy-blocks workgroups")
@@ -314,7 +317,7 @@ def calibrate():
 GEMM_SOURCE = os.path.join(ROOT, "grouped_gemm_weights_amd", "csrc", "grouped_swiglu.hip")
 # the short bench run the counter passes profile (one workload, nothing timed beside it)
 PROFILE_ARGS = ("--config {cfg} --steps 2 --warmup 1 --workloads none --no-cpu-baseline "
-                "--no-library-baseline --alt-steps 0")
+                "--no-library-baseline --alt-steps 0 --graph-steps 0")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_swiglu_traffic.json")
 # kernels of one moe_grouped_swiglu call
 GROUPED_KERNELS = ("plan_kernel", "gemm_stream_kernel", "gemm_wide_kernel")
@@ -423,7 +426,7 @@ def main():
     host_blocks = {}
     result = bench_layer(args, cfg, dev, copy_mode, args.steps, args.warmup, args.alt_steps,
                          headline=True, host_blocks=host_blocks,
-                         remote_on_host=args.remote_pool == "host")
+                         remote_on_host=args.remote_pool == "host", graph_steps=args.graph_steps)
     # the other R1 workloads in the same run, each timed as above (default options), so the
     # prefill MFMA fractions and the pipeline's overlap figures sit beside the headline
     names = [w for w in args.workloads.split(",") if w and w != "none"]
@@ -519,7 +522,7 @@ def pipeline_summary(r):
 
 
 def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=False,
-                host_blocks=None, remote_on_host=False):
+                host_blocks=None, remote_on_host=False, graph_steps=0):
     """One MoE layer step timed over ``steps`` steps; returns its record.  With ``headline``
     the record also carries the input digests and the layer output (for the CPU comparison),
     and host copies of the routed experts' blocks are left in ``host_blocks``."""
@@ -627,6 +630,27 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
                "ms_per_step": round(alt_s * 1e3, 3), "tokens_per_s": round(cfg.T / alt_s, 1)}
         L.copy_mode = copy_mode
 
+    graph_rec = None
+    if on_device and graph_steps > 0:
+        # the same step captured into one HIP graph per half and replayed (not the reported
+        # value): the replays must reproduce the eager step's y bit for bit
+        y_eager = L.y.clone()
+        graphs = [L.capture_step(h) for h in range(2)]
+        for gr in graphs:
+            gr.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(L.y, y_eager))
+        tg = time.perf_counter()
+        for i in range(graph_steps):
+            graphs[i % 2].replay()
+        torch.cuda.synchronize()
+        g_s = (time.perf_counter() - tg) / graph_steps
+        same = same and bool(torch.equal(L.y, y_eager))
+        assert L.read_status() == 0, "device status set during the graph replays"
+        graph_rec = {"steps": graph_steps, "ms_per_step": round(g_s * 1e3, 4),
+                     "tokens_per_s": round(cfg.T / g_s, 1), "y_bit_equal_to_eager": same}
+        del graphs
+
     el = lambda a, b: float(np.mean([B.moe_event_elapsed_ms(ev[a][i], ev[b][i]) for i in range(nev)]))
     if nch > 0:
         n_calls = nch + 1
@@ -718,6 +742,8 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
     }
     if alt is not None:
         result["other_copy_engine"] = alt
+    if graph_rec is not None:
+        result["graph_replay"] = graph_rec
     if args.library_baseline and not remote_on_host:
         lb = library_baseline(L, cfg)
         lb["grouped_kernel_speedup"] = round(lb["ms"] / gemm_ms, 3)

@@ -235,15 +235,33 @@ class MoELayer:
         read-back.  Call after route_permute."""
         cfg = self.cfg
         local = self.stitched_local_pools[half] if self.stitched_local_pools else self.local_pool
+        # the copy stream's first operation is the wait for the permute, so a capture of the step
+        # on the compute stream takes the copy stream's work in too
         B.moe_event_record(self.counts_ready, self.compute_stream)
+        B.moe_stream_wait_event(self.copy_stream, self.counts_ready)
         B.moe_merge_weights(local, range(cfg.n_local), self.wbufs[half], self.copy_stream,
                             wait_free=self.free[half] if wait_free else None, ready=None,
                             copy_mode=self.copy_mode)
         kernel = (self.copy_mode & 0xFF) == B.MOE_COPY_KERNEL
         B.moe_prefetch_routed(self.remote_pool, self.counts, self.wbufs[half], self.copy_stream,
-                              counts_ready=self.counts_ready, ready=self.ready[half],
+                              ready=self.ready[half],
                               max_blocks=(self.copy_mode >> 8) if kernel else 0)
         self.last_ids = None                  # the expert set never reaches the host
+
+    def capture_step(self, half: int = 0) -> "torch.cuda.CUDAGraph":
+        """One device-routed layer step (route, permute, merge, routed pull, grouped GEMM,
+        combine) captured into a HIP graph on this layer's compute stream, the copy stream's
+        work forked into it by the permute's event and joined by the half's ready event.
+        replay() reruns the step on whatever x and logits hold (set_inputs writes them in
+        place).  The half's free event is not waited for inside the graph: replays on one
+        stream run one after another, and the caller must not fill this half from elsewhere
+        while a replay runs."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.compute_stream, capture_error_mode="relaxed"):
+            self.route_permute()
+            self.fill_half_routed_on_device(half, wait_free=False)
+            self.expert_compute(half)
+        return g
 
     def expert_compute(self, half: int) -> None:
         """Compute stream: wait for the half, grouped SwiGLU GEMM, combine, release the half."""

@@ -109,15 +109,17 @@ def check_routing(cfg, out, logits):
     return idx, w, src_of, row_of
 
 
-def check_full(cfg, L, layer: int = 0):
-    """Whole-layer oracle on every token (small shapes)."""
+def check_full(cfg, L, layer: int = 0, check_xperm: bool = True):
+    """Whole-layer oracle on every token (small shapes); x_perm bitwise unless the layer
+    gathers its rows on load (then x_perm is never written)."""
     out = L.outputs()
     assert out["status"] == 0, f"device status {out['status']}"
     x = synth.activations(cfg, layer)
     logits = synth.logits(cfg, layer)
     check_routing(cfg, out, logits)
     ref = O.moe_layer(x, logits, cfg.k, weights_fn(L), cfg.H, cfg.I, round_h=cfg.dtype == "bf16")
-    assert out["x_perm"].tobytes() == np.asarray(ref["x_perm"]).tobytes()
+    if check_xperm:
+        assert out["x_perm"].tobytes() == np.asarray(ref["x_perm"]).tobytes()
     tol = TOL[cfg.dtype]
     e_yp = rel_err(out["y_perm"], ref["y_perm"])
     e_y = rel_err(out["y"], ref["y"])

@@ -378,6 +378,38 @@ def test_device_routed_pull(T, H, I, E, k, n_local, zipf, stitched):
         L.close()
 
 
+@pytest.mark.parametrize("stitched", [False, True], ids=["copy-merge", "stitched-merge"])
+def test_device_routed_step_graph_replay(stitched):
+    """The whole device-routed step captured into a HIP graph: four replays, with eager work
+    and synchronisations between them, each bit-equal to the eager step; then new inputs
+    written in place and one more replay checked against the oracle."""
+    cfg = synth.MoEConfig("bf16_graph_step", T=24, H=1024, I=256, E=32, k=4, dtype="bf16",
+                          n_local=8, seed=77, zipf_s=1.1)
+    log(f"case {cfg.name} stitched={stitched}")
+    L = build_layer(cfg, stitched=stitched, fused_gather=True)
+    try:
+        L.forward(half=0, remote="device")
+        L.synchronize()
+        check_full(cfg, L, check_xperm=False)
+        y0 = L.y.clone()
+        g = L.capture_step(half=0)
+        for r in range(4):
+            L.y.fill_(float("nan"))           # eager work between replays
+            L.y_perm.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(L.y, y0), f"replay {r}"
+        L.set_inputs(synth.activations(cfg, 1), synth.logits(cfg, 1))
+        g.replay()
+        torch.cuda.synchronize()
+        _check_device_slot_map(cfg, L, 0, check_bytes=True)
+        check_full(cfg, L, layer=1, check_xperm=False)
+        del g
+    finally:
+        L.close()
+
+
 def test_merged_buffer_bytes_and_slot_map():
     cfg = synth.MoEConfig("bf16_merge", T=40, H=64, I=32, E=20, k=3, dtype="bf16", n_local=5, seed=3)
     L = build_layer(cfg)
