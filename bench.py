@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--graph-steps", type=int, default=20,
                    help="headline with --remote device: also replay the step captured into a HIP "
                         "graph this many times (0: skip); reported beside the value, not as it")
+    p.add_argument("--cpu-sample-experts", type=int, default=32,
+                   help="prefill workloads: time the oracle's grouped step on this many of the "
+                        "layer's active experts (0: skip)")
     p.add_argument("--copy-mode", choices=["sdma", "any", "kernel"], default="kernel",
                    help="any: hipMemcpyDefault (the runtime's copy path); sdma: the no-compute-unit "
                         "copy kind; kernel: the library's copy kernel on --copy-blocks workgroups")
@@ -159,6 +162,36 @@ def cpu_baseline_bulk(cfg, blocks, y_gpu, single_thread_tokens=0):
         tiny[name] = {"value": round(tc.T / d2, 1), "unit": "tokens/s", "ms": round(d2 * 1e3, 3)}
     out["tiny_fp32_t64"] = tiny
     return out
+
+
+def cpu_baseline_sample(cfg, s):
+    """The oracle's bulk float32 grouped SwiGLU step on a seeded sample of a prefill layer's
+    active experts, each with all its rows: the step that holds nearly all of the layer's
+    work, on a sample, since the oracle decodes every expert's weights from bf16 one at a time
+    (a whole 256-expert layer is about a minute of CPU).  tokens/s = T * (sample rows / R) /
+    time.  The GPU's y_perm rows of the same experts are compared with it (max|err|/RMS)."""
+    import numpy as np
+    from oracle import moe as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    blocks = s["blocks"]
+    t0 = time.perf_counter()
+    y = O.grouped_swiglu(s["xp"], s["off"], lambda i: blocks[i], cfg.H, cfg.I,
+                         round_h=cfg.dtype == "bf16", dtype=np.float32)
+    dt = time.perf_counter() - t0
+    ref = y.astype(np.float64)
+    err = float(np.max(np.abs(np.asarray(s["yp"], np.float64) - ref)) / np.sqrt(np.mean(ref ** 2)))
+    rows = int(s["off"][-1])
+    return {"value": round(cfg.T * rows / s["R"] / dt, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(blocks)} of the layer's {s['n_active']} active experts (seeded), each "
+                      f"with all its rows ({rows} of {s['R']} assignments), through the oracle's "
+                      f"bulk float32 grouped SwiGLU step; tokens/s = T * rows / R / time; "
+                      f"{dt:.1f} s",
+            "experts": s["experts"], "gpu_vs_cpu_max_err_over_rms": round(err, 6)}
 
 
 def _cpu_model():
@@ -445,8 +478,11 @@ def main():
                 r = bench_layer(ha, c, dev, copy_mode, 3, 1, 0, remote_on_host=True)
                 wl[name] = layer_summary(r)
             elif c.layers == 1:
-                r = bench_layer(args, c, dev, copy_mode, args.workload_steps, 2, 0)
+                ns = 0 if args.no_cpu_baseline else args.cpu_sample_experts
+                r = bench_layer(args, c, dev, copy_mode, args.workload_steps, 2, 0, cpu_sample=ns)
                 wl[name] = layer_summary(r)
+                if "_cpu_sample" in r:
+                    wl[name]["cpu_baseline"] = cpu_baseline_sample(c, r.pop("_cpu_sample"))
             else:
                 pa = argparse.Namespace(**vars(args))
                 pa.steps, pa.warmup = args.pipeline_steps, 1
@@ -522,10 +558,13 @@ def pipeline_summary(r):
 
 
 def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=False,
-                host_blocks=None, remote_on_host=False, graph_steps=0):
+                host_blocks=None, remote_on_host=False, graph_steps=0, cpu_sample=0):
     """One MoE layer step timed over ``steps`` steps; returns its record.  With ``headline``
     the record also carries the input digests and the layer output (for the CPU comparison),
-    and host copies of the routed experts' blocks are left in ``host_blocks``."""
+    and host copies of the routed experts' blocks are left in ``host_blocks``.  With
+    ``cpu_sample`` > 0 it carries, under ``_cpu_sample``, a seeded sample of that many active
+    experts: their gathered rows, weight blocks and the GPU's y_perm rows (taken after the
+    timed region)."""
     import numpy as np
     import torch
     from grouped_gemm_weights_amd import binding as B
@@ -748,6 +787,21 @@ def bench_layer(args, cfg, dev, copy_mode, steps, warmup, alt_steps, headline=Fa
         lb = library_baseline(L, cfg)
         lb["grouped_kernel_speedup"] = round(lb["ms"] / gemm_ms, 3)
         result["library_baseline"] = lb
+    if cpu_sample > 0 and not comb:
+        offs = L.offsets.cpu().numpy()
+        src_of = L.src_of.cpu().numpy()
+        active = np.nonzero(counts)[0]
+        pick = np.sort(np.random.default_rng(cfg.seed + 7).choice(
+            active, size=min(cpu_sample, len(active)), replace=False))
+        x_h = synth.activations(cfg)
+        rows = [np.arange(offs[e], offs[e + 1]) for e in pick]
+        result["_cpu_sample"] = {
+            "experts": [int(e) for e in pick], "n_active": int(len(active)), "R": int(R),
+            "xp": np.concatenate([x_h[src_of[r] // cfg.k] for r in rows]),
+            "off": np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int64),
+            "blocks": [block_to_numpy(L.expert_block(int(e))) for e in pick],
+            "yp": np.concatenate([L.y_perm[int(offs[e]):int(offs[e + 1])].cpu().numpy()
+                                  for e in pick])}
     if headline:
         result["inputs_sha256"] = input_digests(cfg, local, remote)
         result["_y"] = L.y.detach().cpu().numpy()

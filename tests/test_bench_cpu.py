@@ -71,3 +71,30 @@ def test_cpu_baseline_bulk_leg():
     assert r["cores"] >= 1 and r["single_thread"]["value"] > 0
     assert r["gpu_vs_cpu_max_err_over_rms"] <= 1e-5
     assert set(r["tiny_fp32_t64"]) == {"all_threads", "single_thread"}
+
+
+def test_cpu_baseline_sample_leg():
+    """bench.py's sampled cpu_baseline leg of the prefill workloads, on the tiny fp32 layer:
+    the oracle's grouped step over a few experts with all their rows, scaled to tokens/s by
+    the share of assignments, compared with the y_perm rows it is handed (here the float64
+    oracle's own)."""
+    import numpy as np
+    from grouped_gemm_weights_amd import synth
+    from oracle import moe as O
+    cfg = synth.config("tiny_fp32_t64")
+    blocks = synth.pool_np(cfg, 0, range(cfg.E))
+    ref = O.moe_layer(synth.activations(cfg), synth.logits(cfg), cfg.k, lambda e: blocks[e],
+                      cfg.H, cfg.I, False)
+    off, src_of = np.asarray(ref["offsets"]), np.asarray(ref["src_of"])
+    pick = [1, 5, 6]
+    rows = [np.arange(off[e], off[e + 1]) for e in pick]
+    s = {"experts": pick, "n_active": cfg.E, "R": cfg.T * cfg.k,
+         "xp": np.concatenate([synth.activations(cfg)[src_of[r] // cfg.k] for r in rows]),
+         "off": np.concatenate([[0], np.cumsum([len(r) for r in rows])]),
+         "blocks": [blocks[e] for e in pick],
+         "yp": np.concatenate([np.asarray(ref["y_perm"])[r] for r in rows])}
+    r = bench.cpu_baseline_sample(cfg, s)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
+    assert r["experts"] == pick and r["cores"] >= 1
+    assert r["gpu_vs_cpu_max_err_over_rms"] <= 1e-5
+    assert f"({int(s['off'][-1])} of {cfg.T * cfg.k} assignments)" in r["sample"]
