@@ -377,7 +377,6 @@ extern "C" int moe_prefetch_routed(const moe_pool* remote, const int32_t* counts
     return fail(MOE_ERR_ARG, "moe_prefetch_routed: experts [%lld, %lld) need slots up to their "
                 "ids (buffer: %d experts, %d slots)", static_cast<long long>(first),
                 static_cast<long long>(first + n), dst->n_experts, dst->n_slots);
-  if (n > 65535) return fail(MOE_ERR_UNSUPPORTED, "moe_prefetch_routed: %lld experts", static_cast<long long>(n));
   const int64_t eb = dst->expert_bytes;
   if (eb % 16 != 0 || reinterpret_cast<uintptr_t>(remote->base) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(dst->base) % 16 != 0)
