@@ -549,6 +549,32 @@ def test_r1_decode_t64_device_routed_pull():
         L.close()
 
 
+def test_r1_decode_t64_graph_replay():
+    """The R1 decode step captured into one HIP graph per buffer half and replayed: every
+    replay bit-equal to the eager step, and the replayed output checked against the oracle on
+    every row and token."""
+    cfg = synth.config("r1_decode_t64")
+    log(f"case {cfg.name} graph replay")
+    L = build_layer(cfg, stitched=True, fused_gather=True)
+    try:
+        L.forward(half=0, remote="device")
+        L.synchronize()
+        y0 = L.y.clone()
+        graphs = [L.capture_step(h) for h in range(2)]
+        for r in range(4):
+            L.y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graphs[r % 2].replay()
+            torch.cuda.synchronize()
+            assert torch.equal(L.y, y0), f"replay {r}"
+        _check_device_slot_map(cfg, L, 1)
+        _, n = check_rows(cfg, L, range(cfg.R), range(cfg.T), check_xperm=False)
+        assert n == cfg.R
+        del graphs
+    finally:
+        L.close()
+
+
 def test_r1_decode_t64_dwdp3_split():
     """The 3-rank split: 86 local experts, 170 fetched; stitched merge.  Every row and every
     token is checked."""
