@@ -122,6 +122,44 @@ def test_all_tokens_one_expert_and_prefill_tiles():
     assert rel_err(out["y"], ref["y"]) <= TOL["bf16"]
 
 
+def _random_cases(n, seed):
+    """Seeded layer shapes: T, H, I, E, k, the local split, skew, gather and pull modes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 5, 8, 16, 37, 64, 100, 256, 300]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.choice([1, 3, 17, 64, 130, 333, 600]))
+        H = 8 * int(rng.integers(1, 65))
+        I = 8 * int(rng.integers(1, 49))
+        cases.append(dict(T=T, H=H, I=I, E=E, k=k, n_local=int(rng.integers(0, E + 1)),
+                          zipf=float(rng.choice([0.0, 1.1])), fused=bool(rng.integers(0, 2)),
+                          remote=str(rng.choice(["routed", "device", "all"])), seed=int(seed * 100 + i)))
+    return cases
+
+
+def test_random_layer_shapes():
+    """Forty seeded layer shapes, each checked against the whole-layer oracle on every token:
+    H and I any multiples of 8 up to 512 and 384, E from 1 to 300, k up to 16, T from 1 to
+    600, any local split, uniform or Zipf-skewed routing, x_perm or the fused gather, and the
+    three pull modes."""
+    for c in _random_cases(40, 61):
+        cfg = synth.MoEConfig(f"bf16_rand{c['seed']}", T=c["T"], H=c["H"], I=c["I"], E=c["E"],
+                              k=c["k"], dtype="bf16", n_local=c["n_local"], seed=c["seed"],
+                              zipf_s=c["zipf"] or None)
+        log(f"case {cfg.name}: T={c['T']} H={c['H']} I={c['I']} E={c['E']} k={c['k']} "
+            f"n_local={c['n_local']} zipf={c['zipf']} fused={c['fused']} remote={c['remote']}")
+        L = build_layer(cfg, fused_gather=c["fused"])
+        try:
+            L.forward(half=0, remote=c["remote"])
+            L.synchronize()
+            check_full(cfg, L, check_xperm=not c["fused"])
+        finally:
+            L.close()
+        del L
+        gc.collect()
+
+
 def _tied_logits(cfg, seed):
     """Logits with ties everywhere: N(0,1) rounded to multiples of 0.5, plus rows of one repeated
     value, rows of +0.0 and -0.0 mixed (equal under the routing order), rows where a run of
