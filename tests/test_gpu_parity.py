@@ -160,6 +160,33 @@ def test_random_layer_shapes():
         gc.collect()
 
 
+def test_random_fp32_layer_shapes():
+    """Sixteen seeded fp32 layers of any H and I (1 to 300, so expert blocks of any byte size),
+    each checked against the whole-layer oracle on every token at the fp32 tolerance; the
+    device-routed pull where the blocks are whole 16-byte words, else the host-routed one."""
+    rng = np.random.default_rng(62)
+    for i in range(16):
+        E = int(rng.choice([1, 3, 8, 33, 100]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T, H, I = int(rng.choice([1, 5, 40, 129])), int(rng.integers(1, 301)), int(rng.integers(1, 301))
+        remote = "device" if (3 * H * I * 4) % 16 == 0 else str(rng.choice(["routed", "all"]))
+        cfg = synth.MoEConfig(f"f32_rand{6200 + i}", T=T, H=H, I=I, E=E, k=k, dtype="f32",
+                              n_local=int(rng.integers(0, E + 1)), seed=6200 + i,
+                              zipf_s=float(rng.choice([0.0, 1.1])) or None)
+        fused = bool(rng.integers(0, 2))
+        log(f"case {cfg.name}: T={T} H={H} I={I} E={E} k={k} n_local={cfg.n_local} "
+            f"fused={fused} remote={remote}")
+        L = build_layer(cfg, fused_gather=fused)
+        try:
+            L.forward(half=0, remote=remote)
+            L.synchronize()
+            check_full(cfg, L, check_xperm=not fused)
+        finally:
+            L.close()
+        del L
+        gc.collect()
+
+
 def _tied_logits(cfg, seed):
     """Logits with ties everywhere: N(0,1) rounded to multiples of 0.5, plus rows of one repeated
     value, rows of +0.0 and -0.0 mixed (equal under the routing order), rows where a run of
