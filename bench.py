@@ -44,6 +44,9 @@ def parse():
                    help="prefetch only the routed remote experts (device: picked on the device "
                         "from the counts, nothing read back; routed: after a count read-back), "
                         "or the whole remote share")
+    p.add_argument("--pipeline-graph-steps", type=int, default=3,
+                   help="pipelines: also replay the pass captured into one HIP graph this many "
+                        "times (0: skip); reported beside the value, not as it")
     p.add_argument("--graph-steps", type=int, default=20,
                    help="headline with --remote device: also replay the step captured into a HIP "
                         "graph this many times (0: skip); reported beside the value, not as it")
@@ -259,6 +262,28 @@ def bench_pipeline(args, cfg, dev, copy_mode):
     C_alone = [el(sev["d0"][l], sev["m1"][l]) for l in range(n)]
     P_alone = [el(sev["c0"][l], sev["c1"][l]) for l in range(n)]
     copy_bytes = (cfg.E - (cfg.n_local if P.stitched else 0)) * synth.expert_block_bytes(cfg)
+    graph_rec = None
+    gsteps = getattr(args, "pipeline_graph_steps", 0)
+    if gsteps > 0 and not split:
+        # the pipelined pass captured into one HIP graph and replayed (not the reported value):
+        # each replay must reproduce the eager pass's final residual stream bit for bit
+        P.forward()
+        torch.cuda.synchronize()
+        x_eager = P.x.clone()
+        g = P.capture()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(P.x, x_eager))
+        tg = time.perf_counter()
+        for _ in range(gsteps):
+            g.replay()
+        torch.cuda.synchronize()
+        g_s = (time.perf_counter() - tg) / gsteps
+        same = same and bool(torch.equal(P.x, x_eager))
+        assert P.L.read_status() == 0, "device status set during the graph replays"
+        graph_rec = {"passes": gsteps, "ms_per_pass": round(g_s * 1e3, 3),
+                     "tokens_per_s": round(cfg.T / g_s, 2), "x_bit_equal_to_eager": same}
+        del g
     P.close()
     for e in [e for ev in evs + [sev] for lst in ev.values() for e in lst]:
         B.moe_event_destroy(e)
@@ -326,6 +351,7 @@ def bench_pipeline(args, cfg, dev, copy_mode):
             "hidden_fraction_definition": "1 - stall/prefetch: time the compute stream waits for "
                                           "the copy, not the slowdown the copy causes",
         },
+        "graph_replay": graph_rec,
     }
 
 
@@ -552,6 +578,8 @@ def pipeline_summary(r):
     out = {"value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"],
            "steps": r["steps"], "roofline": r["roofline"]}
     out.update(r["pipeline"])
+    if r.get("graph_replay") is not None:
+        out["graph_replay"] = r["graph_replay"]
     out["config"] = {k: r["config"][k] for k in ("layers", "tokens", "merge", "gather",
                                                   "copy_engine", "sdma_experts", "pull_chunks")}
     return out

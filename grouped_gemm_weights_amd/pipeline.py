@@ -226,6 +226,31 @@ class MoEPipeline:
                 layer_hook(l)
             self.residual()
 
+    def capture(self) -> "torch.cuda.CUDAGraph":
+        """The pipelined pass over all layers captured into one HIP graph on the compute
+        stream: the copy stream is forked in by an event at the start and joined back by the
+        last layer's ready event.  Inside one pass the first two fills find their halves
+        unused, so only later fills wait for a half's free event (recorded by the pass
+        itself); replays on one stream run one after another.  replay() recomputes x from x0.
+        The split pull is not captured."""
+        assert not self.split, "the split pull is not captured"
+        L, cs, ps = self.L, self.L.compute_stream, self.L.copy_stream
+        if getattr(self, "_fork", None) is None:
+            self._fork = B.moe_event_create(False)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs, capture_error_mode="relaxed"):
+            self.reset()
+            B.moe_event_record(self._fork, cs)
+            B.moe_stream_wait_event(ps, self._fork)
+            self.fill(0, wait_free=False)
+            for l in range(self.n):
+                self.dense(l)
+                if l + 1 < self.n:
+                    self.fill(l + 1, wait_free=l + 1 >= 2)
+                self.moe(l)
+                self.residual()
+        return g
+
     def forward_serial(self, ev: Optional[Dict[str, list]] = None) -> None:
         """Each layer's copies finish before its compute starts (no overlap): the compute
         time alone, for the contention-slowdown figure."""
@@ -256,6 +281,9 @@ class MoEPipeline:
             for e in lst:
                 B.moe_event_destroy(e)
         self.part_ready = []
+        if getattr(self, "_fork", None) is not None:
+            B.moe_event_destroy(self._fork)
+            self._fork = None
         self.L.close()
         for va, sizes in self._ranges:
             B.moe_vmm_unmap(va, sizes)

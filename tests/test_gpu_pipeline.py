@@ -182,6 +182,57 @@ def _check_pipeline(cfg, P, block_to_numpy, n_tokens=16):
     assert e_end <= TOL["bf16"] and norm_end <= TOL["bf16"]
 
 
+def _graph_replays_match(P, replays=3):
+    """Eager pass, then the pass captured and replayed with eager work between replays: the
+    final residual stream of every replay bit-equal to the eager pass's."""
+    P.forward()
+    P.synchronize()
+    x_eager = P.x.clone()
+    g = P.capture()
+    for r in range(replays):
+        P.x.fill_(float("nan"))                      # eager work between replays
+        P.L.y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(P.x, x_eager), f"replay {r}"
+    assert P.L.read_status() == 0
+    del g
+    return x_eager
+
+
+def test_small_pipeline_graph_replay():
+    """The three-layer pipeline captured into one HIP graph: every replay bit-equal to the
+    eager pass, which is itself checked against the oracle on every token of every layer."""
+    from grouped_gemm_weights_amd.layer import block_to_numpy
+    from grouped_gemm_weights_amd.pipeline import MoEPipeline
+    cfg = synth.MoEConfig("pipe_small_graph", T=200, H=256, I=128, E=16, k=4, dtype="bf16",
+                          n_local=4, seed=72, layers=3, dense_standin=True)
+    log(f"case {cfg.name}")
+    P = MoEPipeline(cfg, stitched=False)
+    try:
+        _graph_replays_match(P)
+        _check_pipeline(cfg, P, block_to_numpy, n_tokens=cfg.T)
+    finally:
+        P.close()
+
+
+def test_r1_pipeline_6x4096_graph_replay():
+    """The R1 6 x 4096 pipeline (stitched merge, fused gather) captured into one HIP graph and
+    replayed: every replay's final residual stream bit-equal to the eager pass."""
+    from grouped_gemm_weights_amd.pipeline import MoEPipeline
+    cfg = synth.config("r1_pipeline_6x4096")
+    log(f"case {cfg.name} graph replay")
+    P = MoEPipeline(cfg, stitched=True, fused_gather=True)
+    try:
+        _graph_replays_match(P)
+    finally:
+        P.close()
+        del P
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
 def test_pipeline_event_timeline():
     """The per-layer schedule (explainer, prefetch-schedule and per-layer latency panels) read
     off the events of a pipelined pass over the 6 x 4096 workload: MoE block l starts only
