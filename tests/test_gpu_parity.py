@@ -358,21 +358,24 @@ def test_late_prefetch_is_waited_for():
     assert t_late - t_base >= 0.5 * delay
 
 
-def test_injected_prefetch_fault_surfaces_and_recovers(monkeypatch):
+@pytest.mark.parametrize("remote", ["routed", "device"])
+def test_injected_prefetch_fault_surfaces_and_recovers(monkeypatch, remote):
     """MOE_INJECT_FAULT=prefetch: the layer step raises the library's error instead of running
-    the GEMM on a half that was never filled; without it the next step is correct."""
+    the GEMM on a half that was never filled (host-routed pull, or the device-routed one);
+    without it the next step is correct."""
     from grouped_gemm_weights_amd import binding as B
     cfg = synth.MoEConfig("bf16_fault", T=64, H=128, I=64, E=12, k=3, dtype="bf16", n_local=3,
                           seed=27)
-    log(f"case {cfg.name}")
+    log(f"case {cfg.name} remote={remote}")
     L = build_layer(cfg)
     monkeypatch.setenv("MOE_INJECT_FAULT", "prefetch")
     with pytest.raises(B.MoEError) as e:
-        L.forward(half=0)
+        L.forward(half=0, remote=remote)
     assert e.value.code == B.MOE_ERR_HIP
+    assert ("moe_prefetch_routed" if remote == "device" else "moe_prefetch_layer") in str(e.value)
     monkeypatch.delenv("MOE_INJECT_FAULT")
     L.synchronize()
-    L.forward(half=0)
+    L.forward(half=0, remote=remote)
     check_full(cfg, L)
 
 
