@@ -255,7 +255,8 @@ class MoELayer:
         replay() reruns the step on whatever x and logits hold (set_inputs writes them in
         place).  The half's free event is not waited for inside the graph: replays on one
         stream run one after another, and the caller must not fill this half from elsewhere
-        while a replay runs."""
+        while a replay runs.  The graph holds this layer's buffers and pools by address: replay
+        it only while the layer is open and its pools are alive."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=self.compute_stream, capture_error_mode="relaxed"):
             self.route_permute()

@@ -232,7 +232,8 @@ class MoEPipeline:
         last layer's ready event.  Inside one pass the first two fills find their halves
         unused, so only later fills wait for a half's free event (recorded by the pass
         itself); replays on one stream run one after another.  replay() recomputes x from x0.
-        The split pull is not captured."""
+        The split pull is not captured.  The graph holds the pipeline's buffers by address:
+        replay it only before close()."""
         assert not self.split, "the split pull is not captured"
         L, cs, ps = self.L, self.L.compute_stream, self.L.copy_stream
         if getattr(self, "_fork", None) is None:
