@@ -181,6 +181,13 @@ constexpr int kMGroup = 4;
 // expert's last tile is usually partial (8K-token Zipf routing: 38 % of the
 // tile rows would be padding), as is every tile of a 4096-token layer.
 //
+// Cache hints: a partial tile is its expert's only reader of the weight panels it
+// streams (the expert's full tiles, if any, run in heavy groups elsewhere), so its
+// weight loads are non-temporal and do not evict the panels a heavy group on the same
+// XCD shares between its m-tiles; the epilogue's stores (h, y_perm) are non-temporal
+// too, as they are far larger than L2 and read back only by the next kernel.  Full
+// tiles' weight loads and every activation load stay cached.
+//
 // The loop is software-pipelined by hand: the operand fragments of K step
 // s + 1 are read from LDS while the MFMAs of step s issue, and every stage's
 // global loads are issued two K iterations before their LDS write (a two-slot
@@ -294,21 +301,26 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
   bf16x8_t pa[MW], pb[NJ], qa[MW], qb[NJ]; // operands of two consecutive K steps
 
   // one global chunk load into ring slot rs (chunk t: A chunks first, then B); past K
-  // the chunk is zero
+  // the chunk is zero.  A and B chunks are separate statements so that the B chunks'
+  // non-temporal hint survives (one load of either kind behind a select on t would be
+  // merged into a plain load before the loop is unrolled)
 #define W_GLD(t, k0, rs)                                                               \
   do {                                                                                 \
-    const uint16_t* src_ = (t) < CHA ? reinterpret_cast<const uint16_t*>(              \
-                                           a_base + (a_off[(t) % CHA] + 2u * (k0)))    \
-                         : ((DUAL && ((t) - CHA) % CHB >= CHB / 2) ? B1 : B0) +        \
-                               (b_off[((t) - CHA) % CHB] + (k0));                      \
-    u32x4_t v_;                                                                        \
-    if (KFULL) {                                                                       \
-      v_ = *reinterpret_cast<const u32x4_t*>(src_);                                    \
+    if ((t) < CHA) {                                                                   \
+      const u32x4_t* src_ = reinterpret_cast<const u32x4_t*>(                          \
+          a_base + (a_off[(t) % CHA] + 2u * (k0)));                                    \
+      u32x4_t v_ = u32x4_t{0, 0, 0, 0};                                                \
+      if (KFULL || (k0) + kc * 8 < K) v_ = *src_;                                      \
+      ra[rs][(t) % CHA] = v_;                                                          \
     } else {                                                                           \
-      v_ = u32x4_t{0, 0, 0, 0};                                                        \
-      if ((k0) + kc * 8 < K) v_ = *reinterpret_cast<const u32x4_t*>(src_);             \
+      const u32x4_t* src_ = reinterpret_cast<const u32x4_t*>(                          \
+          ((DUAL && ((t) - CHA) % CHB >= CHB / 2) ? B1 : B0) +                         \
+          (b_off[((t) - CHA) % CHB] + (k0)));                                          \
+      u32x4_t v_ = u32x4_t{0, 0, 0, 0};                                                \
+      if (KFULL || (k0) + kc * 8 < K)                                                  \
+        v_ = MI ? __builtin_nontemporal_load(src_) : *src_;                            \
+      rb[rs][((t) - CHA) % CHB] = v_;                                                  \
     }                                                                                  \
-    if ((t) < CHA) ra[rs][(t) % CHA] = v_; else rb[rs][((t) - CHA) % CHB] = v_;        \
   } while (0)
 #define W_DSW(t, buf, rs)                                                              \
   do {                                                                                 \
@@ -426,8 +438,8 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
       _Pragma("unroll") for (int j = 0; j < NO; ++j) {                                 \
         if ((CHECK) && cw + j * 32 + lrow >= N) continue;                              \
         const float v = DUAL ? silu_f32(acc[i][j][q]) * acc[i][NO + j][q] : acc[i][j][q]; \
-        if constexpr (DUAL || OUT_BF16) orow[j * 32] = f32_to_bf16(v);                 \
-        else orow[j * 32] = v;                                                         \
+        if constexpr (DUAL || OUT_BF16) __builtin_nontemporal_store(f32_to_bf16(v), orow + j * 32); \
+        else __builtin_nontemporal_store(v, orow + j * 32);                            \
       }                                                                                \
     }                                                                                  \
   } while (0)
