@@ -466,8 +466,8 @@ def main():
         print(json.dumps(calibrate()), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path, every "
+              f"figure is one GPU's share (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
