@@ -165,7 +165,7 @@ __device__ __forceinline__ float silu_f32(float g) {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
-constexpr int kMGroup = 4;
+constexpr int kMGroup = 2;
 
 // ---------------------------------------------------------------------------
 // Prefill tile GEMM, one wave per SIMD: 256 x 256 block tile, 4 waves, 32x32x16
