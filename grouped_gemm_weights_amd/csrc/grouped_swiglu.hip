@@ -566,6 +566,9 @@ struct GemmWide {
 // two superblocks in flight per wave (ping-pong register sets).
 //   DUAL: a wave owns 32 output columns (2 gate + 2 up 16-column MFMA blocks);
 //   !DUAL: 64 output columns (4 blocks).  Four waves per block.
+// Grid: x = column block, y = tile, so an expert's column blocks are dispatched one
+// after another (round-robin over the XCDs) and the chip streams a few experts' weight
+// matrices at a time in long contiguous runs (2-3 % faster than tiles fastest).
 // ---------------------------------------------------------------------------
 
 //   NB  16-column MFMA blocks per wave (DUAL: NB / 2 gate + NB / 2 up blocks)
@@ -581,11 +584,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   constexpr int BCOLS = 4 * WCOLS;
   constexpr int SK = 32 * KS;  // K depth of one register stage
   static_assert(!DUAL || NB % 2 == 0, "gate and up blocks come in pairs");
-  if (static_cast<int>(blockIdx.x) >= *n_tiles) return;
-  const Tile tile = tiles[blockIdx.x];
+  if (static_cast<int>(blockIdx.y) >= *n_tiles) return;
+  const Tile tile = tiles[blockIdx.y];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int c0 = blockIdx.y * BCOLS + wave * WCOLS;
+  const int c0 = blockIdx.x * BCOLS + wave * WCOLS;
   if (c0 >= N) return;
   const int lr = lane & 15, lg = lane >> 4;
 
@@ -687,7 +690,7 @@ struct GemmStream {
                     int K, const Tile* tiles, const int32_t* n_tiles, int64_t grid_tiles, void* out,
                     int ldo, hipStream_t s, Scatter sc = Scatter{nullptr, nullptr, 1, nullptr}) {
     if (grid_tiles <= 0) return MOE_OK;
-    dim3 grid(static_cast<unsigned>(grid_tiles), static_cast<unsigned>(ceil_div(N, BCOLS)));
+    dim3 grid(static_cast<unsigned>(ceil_div(N, BCOLS)), static_cast<unsigned>(grid_tiles));
     if (K % (32 * KS) == 0)
       hipLaunchKernelGGL((gemm_stream_kernel<DUAL, true, NB, KS, COMB>), grid, dim3(256), 0, s, A,
                          lda, a_index, a_div, wbase, expert_bytes, b0_off, b1_off, N, K, tiles,
