@@ -294,9 +294,10 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // stages in flight from global memory: two for tiles of at most 64 rows (their short K
-  // iterations would not cover the latency of one), else one (no registers left for more)
-  constexpr int RING = (MI == 2 || MI == 0) ? 2 : 1;
+  // two stages in flight from global memory for every tile mode (a partial tile's short K
+  // iterations would not cover the latency of one; with one, 65-192-row tiles measured
+  // the same or slightly slower)
+  constexpr int RING = 2;
   u32x4_t ra[RING][CHA], rb[RING][CHB];
   bf16x8_t pa[MW], pb[NJ], qa[MW], qb[NJ]; // operands of two consecutive K steps
 
@@ -380,29 +381,23 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
 #pragma unroll
   for (int t = 0; t < NLD; ++t) W_DSW(t, 0, 0);
 #pragma unroll
-  for (int t = 0; t < NLD; ++t) W_GLD(t, min(1, nk - 1) * BK, 1 % RING);
-  if (RING > 1) {
+  for (int t = 0; t < NLD; ++t) W_GLD(t, min(1, nk - 1) * BK, 1);
 #pragma unroll
-    for (int t = 0; t < NLD; ++t) W_GLD(t, min(2, nk - 1) * BK, 0);
-  }
+  for (int t = 0; t < NLD; ++t) W_GLD(t, min(2, nk - 1) * BK, 0);
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < NRD; ++t) W_DSR(pa, pb, t, 0, 0);
 
   int kt = 0;
-  if (RING == 1) {
-    for (; kt + 1 < nk; ++kt) W_ITER(0);
-  } else {
-    while (kt + 2 < nk) {
-      W_ITER(1 % RING);
-      ++kt;
-      W_ITER(0);
-      ++kt;
-    }
-    if (kt + 1 < nk) {
-      W_ITER(1 % RING);
-      ++kt;
-    }
+  while (kt + 2 < nk) {
+    W_ITER(1);
+    ++kt;
+    W_ITER(0);
+    ++kt;
+  }
+  if (kt + 1 < nk) {
+    W_ITER(1);
+    ++kt;
   }
   // last stage: no LDS writes or loads left
   {
