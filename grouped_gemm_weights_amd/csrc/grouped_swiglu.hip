@@ -559,8 +559,10 @@ struct GemmWide {
 // 32-deep MFMA step), so one load instruction reads 64 contiguous bytes of
 // each of 16 rows.  K is consumed in 128-deep superblocks of four MFMA steps,
 // two superblocks in flight per wave (ping-pong register sets).
-//   DUAL: a wave owns 32 output columns (2 gate + 2 up 16-column MFMA blocks);
-//   !DUAL: 64 output columns (4 blocks).  Four waves per block.
+//   DUAL: a wave owns 16 output columns (1 gate + 1 up 16-column MFMA block);
+//   !DUAL: 32 output columns (2 blocks).  Four waves per block.  At 140-144 registers
+//   three waves fit per SIMD (with 4 blocks per wave, two), which streams 2-3 % faster;
+//   8 blocks, or 64- or 256-deep stages, measured the same or slower.
 // Grid: x = column block, y = tile, so an expert's column blocks are dispatched one
 // after another (round-robin over the XCDs) and the chip streams a few experts' weight
 // matrices at a time in long contiguous runs (2-3 % faster than tiles fastest).
@@ -700,9 +702,9 @@ struct GemmStream {
 };
 
 // decode shapes: gate/up with 2 + 2 blocks per wave, down with 4, 128-deep stages
-using Gemm1Stream = GemmStream<true, 4, 4>;
-using Gemm2Stream = GemmStream<false, 4, 4>;
-using Gemm2StreamComb = GemmStream<false, 4, 4, true>;
+using Gemm1Stream = GemmStream<true, 2, 4>;
+using Gemm2Stream = GemmStream<false, 2, 4>;
+using Gemm2StreamComb = GemmStream<false, 2, 4, true>;
 
 // prefill shapes: 256-row tiles
 using Gemm1Prefill = GemmWide<true, false>;
