@@ -169,11 +169,10 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const u32x4* __restr
 // consecutive chunks (group c % gpe) of pool expert c / gpe.  Workgroups take units
 // c = blockIdx.x, blockIdx.x + gridDim.x, ... and skip those of experts that received no
 // tokens; reading that count is one dependent load before a unit's copies start, so a unit
-// holds several chunks to spread it (one chunk per unit made the pull 7 % slower than the
-// host-routed per-run copies).  The slot map entries of the pool's experts (the slot, or -1
-// for an expert with no tokens, whose slot is left as it was) are written by the first
-// threads of the grid.
-constexpr int kRoutedChunks = 4;
+// holds two chunks to spread it (one chunk or four per unit made the pull 2-3 % slower).
+// The slot map entries of the pool's experts (the slot, or -1 for an expert with no
+// tokens, whose slot is left as it was) are written by the first threads of the grid.
+constexpr int kRoutedChunks = 2;
 
 __global__ __launch_bounds__(kCopyThreads) void copy_routed_kernel(
     const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t eb16, int64_t gpe, int first,
