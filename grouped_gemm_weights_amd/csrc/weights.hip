@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const u32x4* __restr
 }
 
 // The routed pull with the expert set read on the device.  A chunk is the kCopyThreads *
-// kCopyUnroll 16-byte units a workgroup moves at once; work unit c is kRoutedChunks
+// kRoutedUnroll 16-byte units a workgroup moves at once; work unit c is kRoutedChunks
 // consecutive chunks (group c % gpe) of pool expert c / gpe.  Workgroups take units
 // c = blockIdx.x, blockIdx.x + gridDim.x, ... and skip those of experts that received no
 // tokens; reading that count is one dependent load before a unit's copies start, so a unit
@@ -173,11 +173,15 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(const u32x4* __restr
 // The slot map entries of the pool's experts (the slot, or -1 for an expert with no
 // tokens, whose slot is left as it was) are written by the first threads of the grid.
 constexpr int kRoutedChunks = 2;
+// 16-byte loads in flight per thread and chunk: 4 here (64 KB chunks), where 8 made the
+// routed pull 2 % slower; the whole-pool copy kernel above keeps 8, where 4 made it 7 %
+// slower
+constexpr int kRoutedUnroll = 4;
 
 __global__ __launch_bounds__(kCopyThreads) void copy_routed_kernel(
     const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t eb16, int64_t gpe, int first,
     int n, const int32_t* __restrict__ counts, int32_t* __restrict__ slot_of) {
-  constexpr int64_t kChunk = static_cast<int64_t>(kCopyThreads) * kCopyUnroll;
+  constexpr int64_t kChunk = static_cast<int64_t>(kCopyThreads) * kRoutedUnroll;
   const int64_t nthreads = static_cast<int64_t>(gridDim.x) * kCopyThreads;
   for (int64_t q = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x; q < n;
        q += nthreads) {
@@ -194,25 +198,25 @@ __global__ __launch_bounds__(kCopyThreads) void copy_routed_kernel(
     for (int g = 0; g < kRoutedChunks; ++g) {
       const int64_t chunk0 = c0 + g * kChunk;
       const int64_t base = chunk0 + threadIdx.x;
-      u32x4 v[kCopyUnroll];
+      u32x4 v[kRoutedUnroll];
       if (chunk0 + kChunk <= eb16) {
         // a whole chunk (a workgroup-uniform test): straight-line loads, then stores, so the
         // next chunk's loads issue without waiting for these stores
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u)
+        for (int u = 0; u < kRoutedUnroll; ++u)
           v[u] = __builtin_nontemporal_load(from + base + static_cast<int64_t>(u) * kCopyThreads);
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u)
+        for (int u = 0; u < kRoutedUnroll; ++u)
           __builtin_nontemporal_store(v[u], to + base + static_cast<int64_t>(u) * kCopyThreads);
       } else if (chunk0 < eb16) {
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
+        for (int u = 0; u < kRoutedUnroll; ++u) {
           const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
           v[u] = u32x4{0, 0, 0, 0};
           if (i < eb16) v[u] = __builtin_nontemporal_load(from + i);
         }
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
+        for (int u = 0; u < kRoutedUnroll; ++u) {
           const int64_t i = base + static_cast<int64_t>(u) * kCopyThreads;
           if (i < eb16) __builtin_nontemporal_store(v[u], to + i);
         }
@@ -393,7 +397,7 @@ extern "C" int moe_prefetch_routed(const moe_pool* remote, const int32_t* counts
   if (wait_free) MOE_HIP_CHECK(hipStreamWaitEvent(s, as_event(wait_free), 0));
   if (n > 0) {
     const int64_t eb16 = eb / 16;
-    const int64_t gpe = ceil_div64(eb16, static_cast<int64_t>(kCopyThreads) * kCopyUnroll *
+    const int64_t gpe = ceil_div64(eb16, static_cast<int64_t>(kCopyThreads) * kRoutedUnroll *
                                              kRoutedChunks);
     const int64_t units = n * gpe;
     // one workgroup per unit unless bounded (the slot map needs ceil(n / kCopyThreads) at most,
