@@ -160,6 +160,15 @@ __device__ __forceinline__ float silu_f32(float g) {
 // streaming the expert's weights from HBM), so at any time some CUs stream
 // weights while others compute, instead of a hot expert's tiles running
 // together and leaving HBM idle.
+//
+// A hot expert (skewed routing) fills several consecutive heavy groups.  Where
+// 4 (else 2) consecutive groups, aligned to 4 (2) in the heavy list, hold tiles
+// of one expert only, they are regrouped: each takes all 4 kMGroup (2 kMGroup)
+// m-tiles of the run but only a quarter (half) of the n-tiles, so an XCD holds
+// 8 A tiles and 4 weight panels of the gate/up GEMM at a time instead of 2 and
+// 16, and each panel crosses the fabric once per 8 m-tiles rather than per 2
+// (8K tokens under Zipf(1.1) routing: 164 of 235 heavy tiles, the call ~1.5 %
+// faster; uniform routing gives experts 2 full tiles and nothing to regroup).
 // ---------------------------------------------------------------------------
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -491,8 +500,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int gsize = min(kMGroup, (heavy ? n_heavy : n_light) - gi * kMGroup);
   const int rem = local % per_group;
   if (rem >= gsize * n_n) return;
-  const int nt = rem / gsize;
-  const int mt = first + rem % gsize;
+  int nt = rem / gsize;
+  int mt = first + rem % gsize;
+  // a run of 4 (else 2) aligned heavy groups of one expert: the same blocks per group,
+  // span * kMGroup m-tiles by n_n / span n-tiles each (every group of the run takes the
+  // same branch, so the run's tiles are still covered exactly once)
+  if (tiles && heavy) {
+    for (int span = 4; span >= 2; span >>= 1) {
+      if (n_n % span) continue;
+      const int pb = (gi & ~(span - 1)) * kMGroup;
+      if (pb + span * kMGroup <= n_heavy &&
+          tiles[pb].expert == tiles[pb + span * kMGroup - 1].expert) {
+        nt = (gi & (span - 1)) * (n_n / span) + rem / (span * kMGroup);
+        mt = pb + rem % (span * kMGroup);
+        break;
+      }
+    }
+  }
 
   Tile tile;
   if (tiles) {

@@ -292,6 +292,35 @@ def test_prefill_multi_tile_experts(fused):
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
+def test_prefill_hot_expert_runs(fused):
+    """Hot experts whose heavy tiles fill runs of aligned heavy groups, which the prefill GEMM
+    regroups into more m-tiles by fewer n-tiles each: 8 full tiles plus a tail (a run of four
+    groups), 4 plus a tail and 4 (runs of two), 2 plus a tail (no run), with I = 512 and
+    H = 1024 so that both GEMMs have 4 n-tiles and both run lengths apply (k = 1).  Every row
+    is checked."""
+    counts = [2100, 1100, 1024, 700, 3, 0]
+    T = sum(counts)
+    cfg = synth.MoEConfig("bf16_hot_runs", T=T, H=1024, I=512, E=len(counts), k=1, dtype="bf16",
+                          n_local=2, seed=31)
+    log(f"case {cfg.name} fused={fused}")
+    L = build_layer(cfg, fused_gather=fused)
+    expert_of = np.repeat(np.arange(cfg.E), counts)
+    np.random.default_rng(32).shuffle(expert_of)
+    logits = synth.logits(cfg)
+    logits[np.arange(T), expert_of] += 50.0
+    L.set_inputs(synth.activations(cfg), logits)
+    L.forward(half=0)
+    out = L.outputs()
+    assert out["status"] == 0
+    np.testing.assert_array_equal(out["counts"], counts)
+    check_routing(cfg, out, logits)
+    ref = O.moe_layer(synth.activations(cfg), logits, cfg.k, weights_fn(L), cfg.H, cfg.I, True)
+    e_yp, e_y = rel_err(out["y_perm"], ref["y_perm"]), rel_err(out["y"], ref["y"])
+    log(f"{cfg.name}: y_perm err/rms {e_yp:.3e}, y err/rms {e_y:.3e}")
+    assert e_yp <= TOL["bf16"] and e_y <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
 def test_decode_tiles_at_row_boundaries(fused):
     """Decode-path layer (at most 4 rows per expert on average) with expert row counts around
     the 16-row stream tile (1, 15, 16, 17, 32, 33), k = 1; H = 320 and I = 192 give both stream
