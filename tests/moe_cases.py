@@ -215,6 +215,64 @@ def check_rows(cfg, L, rows, tokens, layer: int = 0, x=None, logits=None, check_
     return out, len(rows)
 
 
+def check_every_row(cfg, L, layer: int = 0, x=None, logits=None, check_xperm=True, workers=8,
+                    row_block: int = 8192):
+    """Every row of y_perm and every token of y at any size: routing and permutation bit-exact
+    on all tokens (x_perm bitwise when built); each active expert's rows through the oracle's
+    float64 SwiGLU FFN (its block fetched once on this thread, decoded and multiplied on a
+    worker thread, at most ``workers`` experts in flight, each writing its own rows of the
+    float64 reference); y from the oracle's combine of those rows in j order.  The error is
+    max|err| / RMS over all rows, taken ``row_block`` rows at a time so that no temporary of
+    the full R x H size is made beside the reference."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+
+    out = L.outputs()
+    assert out["status"] == 0, f"device status {out['status']}"
+    x = synth.activations(cfg, layer) if x is None else x
+    logits = synth.logits(cfg, layer) if logits is None else logits
+    idx, w, src_of, row_of = check_routing(cfg, out, logits)
+    xa = np.asarray(x)
+    if check_xperm:
+        assert np.array_equal(out["x_perm"], xa[src_of // cfg.k])
+    offsets = O.expert_offsets(O.expert_counts(idx, cfg.E))
+    R = int(offsets[-1])
+    ref = np.empty((R, cfg.H))
+    round_h = cfg.dtype == "bf16"
+    weights_of = weights_fn(L)
+
+    def work(bits, lo, hi):
+        wg, wu, wd = O.expert_matrices(bits, cfg.H, cfg.I)
+        ref[lo:hi] = O.swiglu_ffn(xa[src_of[lo:hi] // cfg.k], wg, wu, wd, round_h)
+
+    active = [e for e in range(cfg.E) if offsets[e + 1] > offsets[e]]
+    pending = set()
+    with threadpool_limits(limits=2), cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        for e in active:
+            if len(pending) >= workers:
+                done, pending = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+                for f in done:
+                    f.result()
+            pending.add(ex.submit(work, weights_of(e), int(offsets[e]), int(offsets[e + 1])))
+        for f in cf.as_completed(pending):
+            f.result()
+    yp = out["y_perm"]
+    max_err, sumsq = 0.0, 0.0
+    for r0 in range(0, R, row_block):
+        g = yp[r0:r0 + row_block].astype(np.float64)
+        rr = ref[r0:r0 + row_block]
+        max_err = max(max_err, float(np.max(np.abs(g - rr))) if g.size else 0.0)
+        sumsq += float(np.sum(rr * rr))
+    e_yp = max_err / max(np.sqrt(sumsq / max(R * cfg.H, 1)), 1e-300)
+    y_ref = O.combine(ref, row_of, w, cfg.k)
+    e_y = rel_err(out["y"], y_ref)
+    tol = TOL[cfg.dtype]
+    log(f"{cfg.name}: y_perm on every one of {R} rows ({len(active)} experts): err/rms "
+        f"{e_yp:.3e}; y on every one of {cfg.T} tokens: err/rms {e_y:.3e} (tol {tol})")
+    assert e_yp <= tol and e_y <= tol
+    return out, R
+
+
 def tokens_layer(weights_of, x_rows, logits_rows, k, H, I, round_h=True, workers=8):
     """The oracle's layer output for a set of token rows: O.route of their logits, each chosen
     expert's FFN on its tokens (expert_ffn_rows: one decode per expert, experts in parallel),

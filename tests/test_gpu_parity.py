@@ -14,8 +14,9 @@ import gc
 import numpy as np
 import pytest
 
-from moe_cases import (O, TOL, build_layer, check_full, check_routing, check_rows,
-                       check_y_tokens, log, rel_err, synth, tile_boundary_rows, weights_fn)
+from moe_cases import (O, TOL, build_layer, check_every_row, check_full, check_routing,
+                       check_rows, check_y_tokens, log, rel_err, synth, tile_boundary_rows,
+                       weights_fn)
 
 pytestmark = pytest.mark.gpu
 
@@ -746,13 +747,15 @@ def test_fused_gather_tiny_fp32():
 
 
 def test_r1_prefill_t16384_fused_gather():
-    """As bench.py runs it (stitched merge, gather on load): the first and last row of every
-    tile and every 32-row block boundary of every expert, and 64 sampled tokens."""
+    """As bench.py runs it (stitched merge, gather on load, device-routed pull): every one of
+    the 131072 rows of y_perm and every one of the 16384 tokens of y against the oracle."""
     cfg = synth.config("r1_prefill_t16384")
+    log(f"case {cfg.name} fused gather, every row")
     L = build_layer(cfg, stitched=True, fused_gather=True)
     try:
-        L.forward(half=0, remote="all")
-        check_rows(cfg, L, tile_boundary_rows, _sample(cfg.T, 64, 13), check_xperm=False)
+        L.forward(half=0, remote="device")
+        _, n = check_every_row(cfg, L, check_xperm=False)
+        assert n == cfg.R
     finally:
         L.close()
 
@@ -779,14 +782,19 @@ def test_stitched_halves_small():
 @pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
 def test_r1_prefill_t8192_zipf(fused):
     """Skewed routing: a few experts with thousands of rows (full tiles), many with a handful
-    (short tiles).  Every tile's first and last row, every 32-row block boundary, and 64
-    sampled tokens."""
+    (short tiles).  As bench.py runs it (stitched merge, gather on load): every one of the
+    65536 rows of y_perm and every token of y.  With x_perm built by moe_permute: every tile's
+    first and last row, every 32-row block boundary, and 64 sampled tokens."""
     cfg = synth.config("r1_prefill_t8192_zipf")
     log(f"case {cfg.name} fused={fused}")
     L = build_layer(cfg, stitched=fused, fused_gather=fused)
     try:
-        _run(L)
-        out, n = check_rows(cfg, L, tile_boundary_rows, _sample(cfg.T, 64, 2), check_xperm=not fused)
+        _run(L, remote="device" if fused else "routed")
+        if fused:
+            out, n = check_every_row(cfg, L, check_xperm=False)
+            assert n == cfg.R
+        else:
+            out, n = check_rows(cfg, L, tile_boundary_rows, _sample(cfg.T, 64, 2))
         log(f"active experts {int((out['counts'] > 0).sum())}, max rows {int(out['counts'].max())}")
     finally:
         L.close()

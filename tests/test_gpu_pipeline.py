@@ -6,7 +6,8 @@ gather, as bench.py runs it).
 Per layer, the oracle is fed the GPU's own layer input (bf16), as the layer
 outputs are then compared one layer at a time; routing is checked bit-exactly
 on all tokens; the dense block, the MoE output and the residual are checked on
-16 sampled tokens.  Tokens are independent through every block, so the oracle
+16 sampled tokens, and for the last layer of the stitched 6 x 4096 pipeline the
+MoE output of every token.  Tokens are independent through every block, so the oracle
 also runs the whole pipeline for the sampled tokens from the seeded
 input and the final residual stream is compared end to end.
 
@@ -40,7 +41,7 @@ def test_r1_pipeline_6x4096(stitched):
     log(f"case {cfg.name} stitched={stitched}")
     P = MoEPipeline(cfg, stitched=stitched)
     try:
-        _check_pipeline(cfg, P, block_to_numpy)
+        _check_pipeline(cfg, P, block_to_numpy, full_layers=(cfg.layers - 1,) if stitched else ())
     finally:
         P.close()
         del P
@@ -118,7 +119,9 @@ def test_r1_pipeline_4x16384():
         torch.cuda.empty_cache()
 
 
-def _check_pipeline(cfg, P, block_to_numpy, n_tokens=16):
+def _check_pipeline(cfg, P, block_to_numpy, n_tokens=16, full_layers=()):
+    """Per layer on the sampled tokens and end to end; for each layer in ``full_layers`` also
+    the MoE output y of every token, on the GPU's own input of that block."""
     tokens = sorted(np.random.default_rng(6).choice(cfg.T, size=n_tokens, replace=False).tolist())
     n = len(tokens)
     cap = []
@@ -165,6 +168,11 @@ def _check_pipeline(cfg, P, block_to_numpy, n_tokens=16):
         log(f"layer {l}: {n} tokens: dense err/rms {e_a:.2e}, moe err/rms {e_y:.2e}, "
             f"residual err/rms {e_r:.2e}")
         assert e_a <= TOL["bf16"] and e_y <= TOL["bf16"] and e_r <= TOL["bf16"]
+        if l in full_layers:
+            y_all = tokens_layer(weights_of, O.decode(c["a"]), logits, cfg.k, cfg.H, cfg.I)
+            e_all = rel_err(c["y"], y_all)
+            log(f"layer {l}: moe output on every one of {cfg.T} tokens: err/rms {e_all:.2e}")
+            assert e_all <= TOL["bf16"]
     # end to end against the oracle's chain from the seeded input
     got_end = O.decode(x_final[tokens])
     # every layer re-rounds the residual stream to bf16: two correct implementations can land

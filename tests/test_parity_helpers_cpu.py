@@ -1,11 +1,13 @@
 """The full-size GPU checks build their expected values from oracle pieces in parallel
-(tests/moe_cases.py: expert_ffn_rows, tokens_layer, check_rows, tile_boundary_rows).
+(tests/moe_cases.py: expert_ffn_rows, tokens_layer, check_rows, check_every_row,
+tile_boundary_rows).
 These CPU tests pin those helpers: they agree with the oracle's own whole-layer and
 per-token functions, select the rows they claim to, and fail on a planted wrong row."""
 import numpy as np
 import pytest
 
-from moe_cases import O, check_rows, expert_ffn_rows, synth, tile_boundary_rows, tokens_layer
+from moe_cases import (O, check_every_row, check_rows, expert_ffn_rows, synth, tile_boundary_rows,
+                       tokens_layer)
 
 torch = pytest.importorskip("torch")
 
@@ -83,3 +85,21 @@ def test_check_rows_passes_on_oracle_outputs_and_catches_a_wrong_row():
     bad_row = int(offs[e + 1] - 1)                   # the last row of the largest group
     with pytest.raises(AssertionError):
         check_rows(cfg, _FakeLayer(cfg, perturb_row=bad_row), tile_boundary_rows, [0], workers=2)
+
+
+def test_check_every_row_passes_on_oracle_outputs_and_catches_a_wrong_row_or_token():
+    cfg = _cfg()
+    _, n = check_every_row(cfg, _FakeLayer(cfg), workers=3, row_block=7)
+    assert n == cfg.R
+    fake = _FakeLayer(cfg)
+    offs = fake.out["offsets"]
+    e = int(np.argmin(np.where(np.diff(offs) > 0, np.diff(offs), 10 ** 9)))
+    # a middle row of the smallest group, away from any 32-row tile edge
+    bad_row = int((offs[e] + offs[e + 1] - 1) // 2)
+    with pytest.raises(AssertionError):
+        check_every_row(cfg, _FakeLayer(cfg, perturb_row=bad_row), workers=3, row_block=7)
+    bad = _FakeLayer(cfg)
+    rms = np.sqrt(np.mean(bad.out["y"].astype(np.float64) ** 2))
+    bad.out["y"][cfg.T // 2, 5] += np.float32(0.1 * rms)
+    with pytest.raises(AssertionError):
+        check_every_row(cfg, bad, workers=3, row_block=7)
