@@ -15,8 +15,7 @@ import numpy as np
 import pytest
 
 from moe_cases import (O, TOL, build_layer, check_every_row, check_full, check_routing,
-                       check_rows, check_y_tokens, log, rel_err, synth, tile_boundary_rows,
-                       weights_fn)
+                       check_rows, check_y_tokens, log, rel_err, synth, weights_fn)
 
 pytestmark = pytest.mark.gpu
 
@@ -587,10 +586,6 @@ def test_status_nonfinite_logit_and_absent_expert():
 # DeepSeek-R1-shaped workloads at full size
 # ----------------------------------------------------------------------------
 
-def _sample(T, n, seed):
-    return sorted(np.random.default_rng(seed).choice(T, size=n, replace=False).tolist())
-
-
 @pytest.mark.parametrize("stitched", [False, True], ids=["copy-merge", "stitched-merge"])
 def test_r1_decode_t64(stitched):
     cfg = synth.config("r1_decode_t64")
@@ -782,29 +777,29 @@ def test_stitched_halves_small():
 @pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
 def test_r1_prefill_t8192_zipf(fused):
     """Skewed routing: a few experts with thousands of rows (full tiles), many with a handful
-    (short tiles).  As bench.py runs it (stitched merge, gather on load): every one of the
-    65536 rows of y_perm and every token of y.  With x_perm built by moe_permute: every tile's
-    first and last row, every 32-row block boundary, and 64 sampled tokens."""
+    (short tiles).  Every one of the 65536 rows of y_perm and every token of y, as bench.py
+    runs it (stitched merge, gather on load, device-routed pull) and with x_perm built by
+    moe_permute (checked bitwise) and the host-routed pull."""
     cfg = synth.config("r1_prefill_t8192_zipf")
     log(f"case {cfg.name} fused={fused}")
     L = build_layer(cfg, stitched=fused, fused_gather=fused)
     try:
         _run(L, remote="device" if fused else "routed")
-        if fused:
-            out, n = check_every_row(cfg, L, check_xperm=False)
-            assert n == cfg.R
-        else:
-            out, n = check_rows(cfg, L, tile_boundary_rows, _sample(cfg.T, 64, 2))
+        out, n = check_every_row(cfg, L, check_xperm=not fused)
+        assert n == cfg.R
         log(f"active experts {int((out['counts'] > 0).sum())}, max rows {int(out['counts'].max())}")
     finally:
         L.close()
 
 
 def test_r1_prefill_t16384():
+    """Copy merge, x_perm built by moe_permute (checked bitwise), the whole remote share
+    pulled: every row of y_perm and every token of y."""
     cfg = synth.config("r1_prefill_t16384")
     log(f"case {cfg.name}")
     L = _run(build_layer(cfg), remote="all")
-    check_rows(cfg, L, tile_boundary_rows, _sample(cfg.T, 64, 3))
+    _, n = check_every_row(cfg, L)
+    assert n == cfg.R
 
 
 # ----------------------------------------------------------------------------
@@ -861,7 +856,7 @@ def test_combine_in_epilogue_r1_prefill_t16384():
     L = build_layer(cfg, stitched=True, combine_in_epilogue=True)
     try:
         L.forward(half=0, remote="all")
-        check_y_tokens(cfg, L, _sample(cfg.T, 64, 17))
+        check_y_tokens(cfg, L, range(cfg.T))
     finally:
         L.close()
 

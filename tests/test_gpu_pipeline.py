@@ -6,8 +6,8 @@ gather, as bench.py runs it).
 Per layer, the oracle is fed the GPU's own layer input (bf16), as the layer
 outputs are then compared one layer at a time; routing is checked bit-exactly
 on all tokens; the dense block, the MoE output and the residual are checked on
-16 sampled tokens, and for the last layer of the stitched 6 x 4096 pipeline the
-MoE output of every token.  Tokens are independent through every block, so the oracle
+16 sampled tokens; the MoE output is also checked on every token of every layer
+of the stitched 6 x 4096 pipeline and of the last layer of the 4 x 16384 one.  Tokens are independent through every block, so the oracle
 also runs the whole pipeline for the sampled tokens from the seeded
 input and the final residual stream is compared end to end.
 
@@ -41,7 +41,7 @@ def test_r1_pipeline_6x4096(stitched):
     log(f"case {cfg.name} stitched={stitched}")
     P = MoEPipeline(cfg, stitched=stitched)
     try:
-        _check_pipeline(cfg, P, block_to_numpy, full_layers=(cfg.layers - 1,) if stitched else ())
+        _check_pipeline(cfg, P, block_to_numpy, full_layers=range(cfg.layers) if stitched else ())
     finally:
         P.close()
         del P
@@ -104,14 +104,15 @@ def test_small_pipeline_split_pull_full_layers(sdma_experts, chunks):
 
 
 def test_r1_pipeline_4x16384():
-    """Four layers at 16384 tokens each, stitched merge: the same checks as above."""
+    """Four layers at 16384 tokens each, stitched merge: the same checks as above, and the
+    last layer's MoE output on every token."""
     from grouped_gemm_weights_amd.layer import block_to_numpy
     from grouped_gemm_weights_amd.pipeline import MoEPipeline
     cfg = synth.config("r1_pipeline_4x16384")
     log(f"case {cfg.name} stitched=True")
     P = MoEPipeline(cfg, stitched=True, fused_gather=True)
     try:
-        _check_pipeline(cfg, P, block_to_numpy)
+        _check_pipeline(cfg, P, block_to_numpy, full_layers=(cfg.layers - 1,))
     finally:
         P.close()
         del P
