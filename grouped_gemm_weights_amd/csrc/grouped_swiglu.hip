@@ -355,16 +355,19 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
   acc[(t) / NJ][(t) % NJ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                   \
       RA[(t) / NJ], RB[(t) % NJ], acc[(t) / NJ][(t) % NJ], 0, 0, 0)
   // One K step: the MFMAs on (RA, RB); between them, in issue order, the operand reads of
-  // the following step into (NA, NB), and the LDS write of each staged chunk of ring slot
-  // rs followed by the global load that refills it.
-#define W_STEP(RA, RB, NA, NB, rd_buf, rd_s, DO_RD, DO_IO, wbuf, gk0, rs)                \
+  // the following step into (NA, NB), and, for the staged chunks io_lo .. io_hi - 1 of ring
+  // slot rs, the LDS write of each chunk followed by the global load that refills it (the
+  // chunks spread evenly over the step's MFMA slots).
+#define W_STEP(RA, RB, NA, NB, rd_buf, rd_s, DO_RD, io_lo, io_hi, wbuf, gk0, rs)         \
   do {                                                                                 \
     _Pragma("unroll") for (int t = 0; t < NS; ++t) {                                   \
       if (t < NMF) W_MFMA(RA, RB, t);                                                  \
       if ((DO_RD) && t < NRD) W_DSR(NA, NB, t, rd_buf, rd_s);                          \
-      if ((DO_IO) && t < NLD) {                                                        \
-        W_DSW(t, wbuf, rs);                                                            \
-        W_GLD(t, gk0, rs);                                                             \
+      _Pragma("unroll") for (int c = (io_lo); c < (io_hi); ++c) {                      \
+        if ((c - (io_lo)) * NS / ((io_hi) - (io_lo)) == t) {                           \
+          W_DSW(c, wbuf, rs);                                                          \
+          W_GLD(c, gk0, rs);                                                           \
+        }                                                                              \
       }                                                                                \
       __builtin_amdgcn_sched_barrier(0);                                               \
     }                                                                                  \
@@ -372,16 +375,23 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
   // K iteration kt computes stage kt from LDS buffer kt & 1.  Stage s >= 1 waits in ring
   // slot s % RING from its global load, issued RING iterations ahead, until iteration
   // s - 1 writes it to LDS buffer s & 1 and reuses the slot for stage s + RING (past the
-  // last stage the load repeats the last stage and is never used).  Step 3's MFMAs run
-  // after the barrier that publishes stage kt + 1, overlapping the first operand reads.
+  // last stage the load repeats the last stage and is never used).  Buffer kt & 1 ^ 1 is
+  // free from the barrier that ended iteration kt - 1, so the stage's LDS writes (64 KB per
+  // full tile) are spread over the three steps before this iteration's barrier: in one step
+  // they would ask the LDS for about 1.5 times what it moves during that step's MFMAs, on
+  // top of the operand reads.  Step 3's MFMAs run after the barrier that publishes stage
+  // kt + 1, overlapping the first operand reads.  With a K tail (!KFULL) the writes stay in
+  // the last step before the barrier: spread, the tail checks' live ranges spill registers.
+  constexpr int IO1 = KFULL ? NLD / 3 : 0, IO2 = KFULL ? (2 * NLD) / 3 : 0;
 #define W_ITER(rs)                                                                     \
   do {                                                                                 \
     const int cur = kt & 1;                                                            \
-    W_STEP(pa, pb, qa, qb, cur, 1, true, false, 0, 0, 0);                              \
-    W_STEP(qa, qb, pa, pb, cur, 2, true, false, 0, 0, 0);                              \
-    W_STEP(pa, pb, qa, qb, cur, 3, true, true, cur ^ 1, min(kt + 1 + RING, nk - 1) * BK, rs); \
+    const int gk_ = min(kt + 1 + RING, nk - 1) * BK;                                   \
+    W_STEP(pa, pb, qa, qb, cur, 1, true, 0, IO1, cur ^ 1, gk_, rs);                    \
+    W_STEP(qa, qb, pa, pb, cur, 2, true, IO1, IO2, cur ^ 1, gk_, rs);                  \
+    W_STEP(pa, pb, qa, qb, cur, 3, true, IO2, NLD, cur ^ 1, gk_, rs);                  \
     __syncthreads();                                                                   \
-    W_STEP(qa, qb, pa, pb, cur ^ 1, 0, true, false, 0, 0, 0);                          \
+    W_STEP(qa, qb, pa, pb, cur ^ 1, 0, true, 0, 0, 0, 0, 0);                           \
   } while (0)
 
   const int nk = (K + BK - 1) / BK;
@@ -411,10 +421,10 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
   // last stage: no LDS writes or loads left
   {
     const int cur = kt & 1;
-    W_STEP(pa, pb, qa, qb, cur, 1, true, false, 0, 0, 0);
-    W_STEP(qa, qb, pa, pb, cur, 2, true, false, 0, 0, 0);
-    W_STEP(pa, pb, qa, qb, cur, 3, true, false, 0, 0, 0);
-    W_STEP(qa, qb, pa, pb, 0, 0, false, false, 0, 0, 0);
+    W_STEP(pa, pb, qa, qb, cur, 1, true, 0, 0, 0, 0, 0);
+    W_STEP(qa, qb, pa, pb, cur, 2, true, 0, 0, 0, 0, 0);
+    W_STEP(pa, pb, qa, qb, cur, 3, true, 0, 0, 0, 0, 0);
+    W_STEP(qa, qb, pa, pb, 0, 0, false, 0, 0, 0, 0, 0);
   }
 #undef W_ITER
 #undef W_GLD
