@@ -356,15 +356,19 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
       RA[(t) / NJ], RB[(t) % NJ], acc[(t) / NJ][(t) % NJ], 0, 0, 0)
   // One K step: the MFMAs on (RA, RB); between them, in issue order, the operand reads of
   // the following step into (NA, NB), and, for the staged chunks io_lo .. io_hi - 1 of ring
-  // slot rs, the LDS write of each chunk followed by the global load that refills it (the
-  // chunks spread evenly over the step's MFMA slots).
+  // slot rs, the LDS write of each chunk followed by the global load that refills it.  The
+  // reads go into the step's first MFMA slots and the chunks spread evenly over the slots
+  // after them (over all slots when those are too few), so that the LDS does not take
+  // writes and reads in the same stretch of MFMAs (2 % faster than writes spread over all
+  // slots, 3-4 % faster than all writes in one step).
+#define W_SLOT(i, n) (NS - NRD >= (n) ? NRD + (i) * (NS - NRD) / (n) : (i) * NS / (n))
 #define W_STEP(RA, RB, NA, NB, rd_buf, rd_s, DO_RD, io_lo, io_hi, wbuf, gk0, rs)         \
   do {                                                                                 \
     _Pragma("unroll") for (int t = 0; t < NS; ++t) {                                   \
       if (t < NMF) W_MFMA(RA, RB, t);                                                  \
       if ((DO_RD) && t < NRD) W_DSR(NA, NB, t, rd_buf, rd_s);                          \
       _Pragma("unroll") for (int c = (io_lo); c < (io_hi); ++c) {                      \
-        if ((c - (io_lo)) * NS / ((io_hi) - (io_lo)) == t) {                           \
+        if (W_SLOT(c - (io_lo), (io_hi) - (io_lo)) == t) {                            \
           W_DSW(c, wbuf, rs);                                                          \
           W_GLD(c, gk0, rs);                                                           \
         }                                                                              \
@@ -432,6 +436,7 @@ __device__ __forceinline__ void wide_tile(const Tile& tile, int n0, const uint16
 #undef W_DSR
 #undef W_MFMA
 #undef W_STEP
+#undef W_SLOT
 
   // epilogue: element q of a 32x32 block sits at row (q/4)*8 + (lane/32)*4 + q%4, column
   // lane%32.  Offsets run from this lane's first output; a wave whose rows and columns all
