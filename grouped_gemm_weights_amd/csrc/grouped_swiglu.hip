@@ -184,9 +184,11 @@ constexpr int kMGroup = 2;
 // MFMA blocks, all 256 accumulators per lane).  Against an 8-wave split into
 // 128 x 64 quarters this reads a third less LDS per MFMA (each operand fetched
 // from LDS feeds four MFMAs), and LDS bandwidth is what bounds this loop.
-// Partial tiles (at most MI * 32 rows, MI = 2, 4 or 6): the waves split the
+// Partial tiles (at most MI * 32 rows, MI = 1, 2, 4 or 6): the waves split the
 // columns instead and each owns all MI * 32 rows x 64 columns, so the MFMA work
-// of the tile shrinks with its row count rather than idling whole SIMDs.  An
+// of the tile shrinks with its row count rather than idling whole SIMDs (a tile of
+// at most 32 rows, most of an expert's short last tiles under skewed routing, issues
+// half the MFMAs and A stage writes of a 64-row one: 1-2 % off the grouped call).  An
 // expert's last tile is usually partial (8K-token Zipf routing: 38 % of the
 // tile rows would be padding), as is every tile of a 4096-token layer.
 //
@@ -554,8 +556,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wide_tile<DUAL, OUT_BF16, KFULL, 6, COMB>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem, sc);
   else if (tile.rows > 64)
     wide_tile<DUAL, OUT_BF16, KFULL, 4, COMB>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem, sc);
-  else
+  else if (tile.rows > 32)
     wide_tile<DUAL, OUT_BF16, KFULL, 2, COMB>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem, sc);
+  else
+    wide_tile<DUAL, OUT_BF16, KFULL, 1, COMB>(tile, n0, A, lda, a_index, a_div, B0, B1, N, K, out, ldo, smem, sc);
 }
 
 template <bool DUAL, bool OUT_BF16, bool COMB = false>

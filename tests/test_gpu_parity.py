@@ -4,10 +4,8 @@ Every test runs the library on seeded inputs and compares with the oracle
 element by element: bit-exact for routing ids, counts, offsets, the
 permutation and the gathered rows; within the tolerances of tests/moe_cases.py
 for the routing weights and the float outputs.  Shapes span several tiles
-with ragged tails.  The DeepSeek-R1-shaped workloads run at full size: decode
-layers are checked on every row and token, prefill layers on the rows at both
-sides of every 32-row boundary inside each expert (so the first and last row of
-every tile) and on 64 sampled tokens.
+with ragged tails.  The DeepSeek-R1-shaped workloads run at full size and are
+checked on every row of y_perm and every token of y.
 """
 import gc
 
@@ -238,11 +236,11 @@ def test_routing_ties_and_signed_zeros(E, k, H, I):
 
 @pytest.mark.parametrize("fused", [False, True], ids=["x_perm", "fused-gather"])
 def test_prefill_tile_modes_at_row_boundaries(fused):
-    """Expert row counts on both sides of every prefill tile mode (64/128/192-row column-split
-    tiles, full 256-row tiles, and a full tile plus a one-row tail), k = 1 so each count is
-    exact; I = 192 leaves the gate/up GEMM a partial column block, so the epilogue runs both
-    its unchecked (whole waves) and checked stores."""
-    counts = [64, 65, 128, 129, 192, 193, 256, 257]
+    """Expert row counts on both sides of every prefill tile mode (32/64/128/192-row
+    column-split tiles, full 256-row tiles, and a full tile plus a one-row tail), k = 1 so each
+    count is exact; I = 192 leaves the gate/up GEMM a partial column block, so the epilogue
+    runs both its unchecked (whole waves) and checked stores."""
+    counts = [1, 32, 33, 64, 65, 128, 129, 192, 193, 256, 257]
     T = sum(counts)
     cfg = synth.MoEConfig("bf16_tile_modes", T=T, H=256, I=192, E=len(counts), k=1, dtype="bf16",
                           n_local=3, seed=21)
